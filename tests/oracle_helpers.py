@@ -1,0 +1,32 @@
+"""Test-side helpers: build the oracle's host cache from synthetic inputs."""
+import numpy as np
+import torch
+
+import oracle
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    """Raw bit pattern of a bf16/fp16 tensor as a uint16 numpy array (host copy)."""
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def cfg_for(c_bits: int = 4, **kw) -> oracle.Cfg:
+    return oracle.Cfg(c_bits=c_bits, **kw)
+
+
+def oracle_cache(cfg: oracle.Cfg, inp, B: int):
+    """Run the oracle writer over every token of `inp` into fresh host buffers."""
+    D = cfg.d_c + cfg.d_r
+    pages = np.zeros((inp.num_pages, oracle.page_bytes(cfg)), np.uint8)
+    sink = np.zeros((B, max(cfg.n_sink, 1), D), np.uint16)
+    local = np.zeros((B, max(cfg.n_local, 1), D), np.uint16)
+    oracle.write(cfg, u16(inp.c_kv), u16(inp.k_rope), inp.seq_idx.cpu().numpy(),
+                 inp.pos.cpu().numpy(), inp.seq_lens.cpu().numpy(),
+                 inp.page_table.cpu().numpy(), pages, sink, local)
+    return pages, sink, local
+
+
+def oracle_decode(cfg, inp, pages, sink, local, scale, sel=None, p_begin=0, p_end=-1):
+    return oracle.decode(cfg, scale, u16(inp.q_lat), u16(inp.q_rope), pages,
+                         inp.page_table.cpu().numpy(), inp.seq_lens.cpu().numpy(), sink, local,
+                         sel=sel, p_begin=p_begin, p_end=p_end)

@@ -1,0 +1,171 @@
+"""Pins for the oracle's quantizer, packing and page layout.
+
+* brute force: every code is the nearest of the 2^b levels q*s + z (fp64),
+  up to the fp32 evaluation of near-ties;
+* representable groups round-trip exactly; constant groups give zero codes;
+* hand-derived packed bytes (tests/golden) fix the code order and layout.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _levels(s16, z16, bits):
+    s = oracle.f16_bits_to_f64(s16)
+    z = oracle.f16_bits_to_f64(z16)
+    return np.arange(1 << bits) * s + z, s
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("kind", ["normal", "outlier", "tiny", "shifted"])
+def test_codes_are_nearest_level(bits, kind):
+    rng = np.random.default_rng(10 + bits)
+    n_bad = 0
+    for trial in range(400):
+        x = rng.standard_normal(32)
+        if kind == "outlier":
+            x[rng.integers(0, 32)] *= 10.0
+        elif kind == "tiny":
+            x *= 1e-3
+        elif kind == "shifted":
+            x = x * 0.1 + 5.0
+        x = x.astype(np.float32)
+        s16, z16, q = oracle.quantize_group(x, bits)
+        lv, s = _levels(s16, z16, bits)
+        assert s > 0
+        d = np.abs(x.astype(np.float64)[:, None] - lv[None, :])
+        best = np.argmin(d, axis=1)
+        for i in range(32):
+            if q[i] == best[i]:
+                continue
+            # only a near-tie (decided by fp32 rounding of (x - z) / s) may differ
+            gap = abs(d[i, q[i]] - d[i, best[i]])
+            if gap > 1e-5 * s:
+                n_bad += 1
+    assert n_bad == 0
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_reconstruction_error_bound(bits):
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        x = (rng.standard_normal(32) * rng.uniform(0.01, 20)).astype(np.float32)
+        s16, z16, q = oracle.quantize_group(x, bits)
+        lv, s = _levels(s16, z16, bits)
+        xh = lv[q]
+        # within half a step, plus the fp16 rounding of the zero point at the
+        # bottom and of the scale accumulated over 2^b - 1 steps at the top
+        z = oracle.f16_bits_to_f64(z16)
+        slack = abs(float(x.min()) - z) + (1 << bits) * abs(
+            s - (float(x.max()) - float(x.min())) / ((1 << bits) - 1))
+        assert np.all(np.abs(x - xh) <= s / 2 + slack + 1e-12)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_representable_round_trip(bits):
+    rng = np.random.default_rng(4)
+    qmax = (1 << bits) - 1
+    for _ in range(200):
+        e = int(rng.integers(-8, 3))
+        s = 2.0 ** e
+        m = int(rng.integers(-200, 200))
+        z = m * s
+        k = rng.integers(0, qmax + 1, 32)
+        k[rng.integers(0, 32)] = 0
+        k[rng.integers(0, 32)] = qmax
+        if k.min() != 0 or k.max() != qmax:
+            k[0], k[1] = 0, qmax
+        x = (z + k * s).astype(np.float32)
+        s16, z16, q = oracle.quantize_group(x, bits)
+        assert oracle.f16_bits_to_f64(s16) == s
+        assert oracle.f16_bits_to_f64(z16) == z
+        assert np.array_equal(q, k.astype(np.uint8))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("v", [0.0, 1.5, -3.25, 1e-3])
+def test_constant_group(bits, v):
+    x = np.full(32, v, np.float32)
+    s16, z16, q = oracle.quantize_group(x, bits)
+    assert s16 == 0
+    assert z16 == int(np.float16(v).view(np.uint16))
+    assert not q.any()
+
+
+def test_scale_underflow_gives_zero_codes():
+    # range so small that the fp16 scale rounds to zero
+    x = np.full(32, 1.0, np.float32)
+    x[3] = np.nextafter(np.float32(1.0), np.float32(2.0))
+    s16, z16, q = oracle.quantize_group(x, 4)
+    assert s16 == 0 and not q.any()
+
+
+def _read_golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split(":")
+            out[k.strip()] = bytes(int(t, 16) for t in v.split())
+    return out
+
+
+def _write_one(cfg, c_vals, r_vals):
+    def bf(v):
+        import torch
+        return torch.tensor(v, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy(
+        ).view(np.uint16).reshape(1, -1)
+    B, max_pages = 1, 1
+    pages = np.zeros((1, oracle.page_bytes(cfg)), np.uint8)
+    D = cfg.d_c + cfg.d_r
+    sink = np.zeros((B, max(cfg.n_sink, 1), D), np.uint16)
+    local = np.zeros((B, max(cfg.n_local, 1), D), np.uint16)
+    oracle.write(cfg, bf(c_vals), bf(r_vals), [0], [0], [1], np.zeros((1, 1), np.int32), pages,
+                 sink, local)
+    return pages[0]
+
+
+def test_golden_packing_c4r4():
+    cfg = oracle.Cfg(d_c=32, d_r=32, c_bits=4, r_bits=4, group=32, page_size=2, n_sink=0,
+                     n_local=0)
+    vals = [(i % 16) * 0.5 for i in range(32)]
+    page = _write_one(cfg, vals, vals)
+    g = _read_golden("pack_c4r4_tiny.txt")
+    off = oracle.page_regions(cfg)
+    assert off == [0, 2 * 16, 2 * 32, 2 * 36]
+    assert oracle.page_bytes(cfg) == 2 * 40
+    assert bytes(page[off[0]:off[0] + 16]) == g["content_codes"]
+    assert bytes(page[off[1]:off[1] + 16]) == g["rope_codes"]
+    assert bytes(page[off[2]:off[2] + 4]) == g["content_sz"]
+    assert bytes(page[off[3]:off[3] + 4]) == g["rope_sz"]
+    # slot 1 was never written
+    assert not page[16:32].any()
+
+
+def test_golden_packing_c2():
+    cfg = oracle.Cfg(d_c=32, d_r=32, c_bits=2, r_bits=4, group=32, page_size=1, n_sink=0,
+                     n_local=0)
+    vals = [(i % 4) * 0.25 for i in range(32)]
+    page = _write_one(cfg, vals, [0.0] * 32)
+    g = _read_golden("pack_c2_tiny.txt")
+    off = oracle.page_regions(cfg)
+    assert bytes(page[off[0]:off[0] + 8]) == g["content_codes"]
+    assert bytes(page[off[2]:off[2] + 4]) == g["content_sz"]
+
+
+def test_page_sizes_of_the_workload_layouts():
+    # 512 content + 64 RoPE channels, groups of 32, fp16 (scale, zero) per group:
+    # C4R4 = 256 + 32 + 16*4 + 2*4 = 360 B/token, C2R4 = 128 + 32 + 64 + 8 = 232 B/token
+    c4 = oracle.Cfg()
+    c2 = oracle.Cfg(c_bits=2)
+    assert oracle.page_bytes(c4) == 64 * 360 == 23040
+    assert oracle.page_bytes(c2) == 64 * 232 == 14848
+    assert oracle.page_regions(c4) == [0, 16384, 18432, 22528]
+    assert oracle.page_regions(c2) == [0, 8192, 10240, 14336]
