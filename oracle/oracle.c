@@ -18,9 +18,14 @@
  *  Q2 Rounding: fp32 subtraction and correctly rounded fp32 division, RNE
  *     rint, RNE fp32->fp16. Ties go to the even code.
  *  Q3 A group whose fp16 scale is zero gets all-zero codes.
- *  Q4 Code order: within each 32-bit little-endian word of 32/b codes, the
- *     codes of even channels fill the low half-word and those of odd channels
- *     the high half-word (channel 2a+k of the word sits in slot a + k*16/b).
+ *  Q4 Code order (the pages give none; chosen so that one 128-bit load hands
+ *     a GPU lane the same 8-channel sub-block of several groups): a vector of
+ *     n_g groups of 32 channels at b bits is cut into chunks of u = min(n_g, 16/b)
+ *     groups; chunk (ld, j) lies at byte u*b*(4*ld + j) and holds sub-block j
+ *     (channels 8j..8j+7 of each group) of groups u*ld .. u*ld+u-1. Inside a chunk,
+ *     group u*ld + gi sits in 32-bit little-endian word gi / (4/b), code block
+ *     e = gi mod (4/b); channel 8j + 2i + k of the group sits at bit
+ *     16k + b*(4e + i): even channels fill the low half-word, odd ones the high.
  *  Q5 Page layout: page_size token slots, four token-major regions: content
  *     codes, RoPE codes, content (scale, zero) fp16 pairs, RoPE pairs.
  *  Q6 Protection (sink4/local128 of Figure 5 and Table 9; Figure 8): token p
@@ -56,9 +61,12 @@ int orc_check_cfg(const orc_cfg* c) {
   if (!c) return -1;
   if (c->c_bits != 2 && c->c_bits != 4) return -1;
   if (c->r_bits != 2 && c->r_bits != 4) return -1;
-  if (c->group < 16 || c->group % 16 != 0) return -1;
+  if (c->group != 32) return -1; /* the code order works in 8-channel sub-blocks */
   if (c->d_c <= 0 || c->d_c % c->group != 0) return -1;
   if (c->d_r <= 0 || c->d_r % c->group != 0) return -1;
+  /* a chunk must hold at least one whole 32-bit word */
+  if ((c->d_c / 32) * c->c_bits < 4 && c->c_bits == 2) return -1;
+  if ((c->d_r / 32) * c->r_bits < 4 && c->r_bits == 2) return -1;
   if (c->page_size <= 0 || c->n_sink < 0 || c->n_local < 0) return -1;
   return 0;
 }
@@ -191,11 +199,17 @@ size_t orc_page_bytes(const orc_cfg* c) {
               (size_t)(c->d_c / c->group) * 4u + (size_t)(c->d_r / c->group) * 4u);
 }
 
-/* Bit offset of channel k (0 <= k < 32/bits) inside its 32-bit code word. */
-static int code_bit_offset(int k, int bits) {
-  int per_word = 32 / bits;
-  int slot = (k / 2) + (k % 2) * (per_word / 2);
-  return slot * bits;
+/* Byte offset of the 32-bit word and bit offset inside it of channel ch of a
+ * vector of n_g groups of 32 channels stored at `bits` bits (reading Q4). */
+static void code_position(int n_g, int bits, int ch, int* byte_off, int* bit_off) {
+  int g = ch / 32, c = ch % 32;
+  int j = c / 8, i = (c % 8) / 2, k = c % 2;
+  int u = n_g < 16 / bits ? n_g : 16 / bits; /* groups per chunk */
+  int ld = g / u, gi = g % u;
+  int per_word = 4 / bits; /* groups sharing one word */
+  int w = gi / per_word, e = gi % per_word;
+  *byte_off = u * bits * (4 * ld + j) + 4 * w;
+  *bit_off = 16 * k + bits * (4 * e + i);
 }
 
 static void put_u32(uint8_t* p, uint32_t v) {
@@ -228,12 +242,13 @@ static void pack_vector(const uint16_t* in, int d, int bits, int group, uint8_t*
     put_u16(sz_dst + 4 * g, s16);
     put_u16(sz_dst + 4 * g + 2, z16);
   }
-  int per_word = 32 / bits;
-  for (int w = 0; w < d / per_word; ++w) {
-    uint32_t word = 0;
-    for (int k = 0; k < per_word; ++k)
-      word |= (uint32_t)q[w * per_word + k] << code_bit_offset(k, bits);
-    put_u32(code_dst + 4 * w, word);
+  for (int w = 0; w < d * bits / 32; ++w) put_u32(code_dst + 4 * w, 0u);
+  for (int ch = 0; ch < d; ++ch) {
+    int byte_off, bit_off;
+    code_position(d / group, bits, ch, &byte_off, &bit_off);
+    uint32_t word = get_u32(code_dst + byte_off);
+    word |= (uint32_t)q[ch] << bit_off;
+    put_u32(code_dst + byte_off, word);
   }
 }
 
@@ -257,6 +272,8 @@ int orc_write(const orc_cfg* c, int n, const uint16_t* c_kv, const uint16_t* k_r
   const size_t cc = code_bytes(c->d_c, c->c_bits), rc = code_bytes(c->d_r, c->r_bits);
   const size_t cs = (size_t)(c->d_c / c->group) * 4u, rs = (size_t)(c->d_r / c->group) * 4u;
   const int D = c->d_c + c->d_r;
+  /* validate every index first, then write (tokens are independent: each
+   * (sequence, position) appears once, so no two tokens share a slot) */
   for (int t = 0; t < n; ++t) {
     int b = seq_idx[t], p = pos[t];
     if (b < 0 || b >= B) return -1;
@@ -264,6 +281,12 @@ int orc_write(const orc_cfg* c, int n, const uint16_t* c_kv, const uint16_t* k_r
     if (p < 0 || p >= L || p / c->page_size >= max_pages) return -1;
     int64_t page = page_table[(size_t)b * max_pages + p / c->page_size];
     if (page < 0 || page >= num_pages) return -1;
+  }
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < n; ++t) {
+    int b = seq_idx[t], p = pos[t];
+    int L = seq_lens[b];
+    int64_t page = page_table[(size_t)b * max_pages + p / c->page_size];
     int slot = p % c->page_size;
     uint8_t* base = pages + (size_t)page * pb;
     const uint16_t* xc = c_kv + (size_t)t * c->d_c;
@@ -290,11 +313,11 @@ int orc_write(const orc_cfg* c, int n, const uint16_t* c_kv, const uint16_t* k_r
 
 static void unpack_vector(const uint8_t* code_src, const uint8_t* sz_src, int d, int bits,
                           int group, double* out) {
-  int per_word = 32 / bits;
   uint32_t mask = (1u << bits) - 1u;
   for (int i = 0; i < d; ++i) {
-    uint32_t word = get_u32(code_src + 4 * (i / per_word));
-    uint32_t q = (word >> code_bit_offset(i % per_word, bits)) & mask;
+    int byte_off, bit_off;
+    code_position(d / group, bits, i, &byte_off, &bit_off);
+    uint32_t q = (get_u32(code_src + byte_off) >> bit_off) & mask;
     int g = i / group;
     double s = orc_f16_to_f64(get_u16(sz_src + 4 * g));
     double z = orc_f16_to_f64(get_u16(sz_src + 4 * g + 2));

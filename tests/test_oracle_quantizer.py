@@ -133,31 +133,32 @@ def _write_one(cfg, c_vals, r_vals):
 
 
 def test_golden_packing_c4r4():
-    cfg = oracle.Cfg(d_c=32, d_r=32, c_bits=4, r_bits=4, group=32, page_size=2, n_sink=0,
+    cfg = oracle.Cfg(d_c=128, d_r=32, c_bits=4, r_bits=4, group=32, page_size=2, n_sink=0,
                      n_local=0)
-    vals = [(i % 16) * 0.5 for i in range(32)]
-    page = _write_one(cfg, vals, vals)
+    cvals = [((c % 32) + 3 * (c // 32)) % 16 * 0.5 for c in range(128)]
+    rvals = [(i % 16) * 0.5 for i in range(32)]
+    page = _write_one(cfg, cvals, rvals)
     g = _read_golden("pack_c4r4_tiny.txt")
     off = oracle.page_regions(cfg)
-    assert off == [0, 2 * 16, 2 * 32, 2 * 36]
-    assert oracle.page_bytes(cfg) == 2 * 40
-    assert bytes(page[off[0]:off[0] + 16]) == g["content_codes"]
+    assert off == [0, 2 * 64, 2 * 80, 2 * 96]
+    assert oracle.page_bytes(cfg) == 2 * 100
+    assert bytes(page[off[0]:off[0] + 64]) == g["content_codes"]
     assert bytes(page[off[1]:off[1] + 16]) == g["rope_codes"]
-    assert bytes(page[off[2]:off[2] + 4]) == g["content_sz"]
+    assert bytes(page[off[2]:off[2] + 16]) == g["content_sz"]
     assert bytes(page[off[3]:off[3] + 4]) == g["rope_sz"]
     # slot 1 was never written
-    assert not page[16:32].any()
+    assert not page[64:128].any()
 
 
 def test_golden_packing_c2():
-    cfg = oracle.Cfg(d_c=32, d_r=32, c_bits=2, r_bits=4, group=32, page_size=1, n_sink=0,
+    cfg = oracle.Cfg(d_c=64, d_r=32, c_bits=2, r_bits=4, group=32, page_size=1, n_sink=0,
                      n_local=0)
-    vals = [(i % 4) * 0.25 for i in range(32)]
+    vals = [(c % 4) * 0.25 for c in range(32)] + [(c // 8) * 0.25 for c in range(32)]
     page = _write_one(cfg, vals, [0.0] * 32)
     g = _read_golden("pack_c2_tiny.txt")
     off = oracle.page_regions(cfg)
-    assert bytes(page[off[0]:off[0] + 8]) == g["content_codes"]
-    assert bytes(page[off[2]:off[2] + 4]) == g["content_sz"]
+    assert bytes(page[off[0]:off[0] + 16]) == g["content_codes"]
+    assert bytes(page[off[2]:off[2] + 8]) == g["content_sz"]
 
 
 def test_page_sizes_of_the_workload_layouts():
