@@ -1,0 +1,209 @@
+"""ctypes binding over libmla_lowbit.so (declarations: include/mla_lowbit.h).
+
+Argument marshalling only: every step of the write and decode runs in the HIP
+kernels. There is no CPU fallback; a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_lowbit.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
+
+
+class MlaLowbitError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed with {code}: {strerror(code)}")
+
+
+class _CCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("d_c", "d_r", "c_bits", "r_bits", "group", "page_size", "n_sink", "n_local")]
+
+
+@dataclass(frozen=True)
+class Config:
+    """Cache geometry (mla_lowbit_config)."""
+    d_c: int = 512
+    d_r: int = 64
+    c_bits: int = 4
+    r_bits: int = 4
+    group: int = 32
+    page_size: int = 64
+    n_sink: int = 4
+    n_local: int = 128
+
+    def c(self) -> _CCfg:
+        return _CCfg(self.d_c, self.d_r, self.c_bits, self.r_bits, self.group, self.page_size,
+                     self.n_sink, self.n_local)
+
+
+C4R4 = Config(c_bits=4)
+C2R4 = Config(c_bits=2)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                "g.build()'` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.mla_lowbit_version.argtypes = []
+        L.mla_lowbit_version.restype = i32
+        L.mla_lowbit_strerror.argtypes = [i32]
+        L.mla_lowbit_strerror.restype = ctypes.c_char_p
+        L.mla_lowbit_check_config.argtypes = [P]
+        L.mla_lowbit_check_config.restype = i32
+        L.mla_lowbit_page_bytes.argtypes = [P]
+        L.mla_lowbit_page_bytes.restype = sz
+        L.mla_lowbit_decode_workspace_bytes.argtypes = [P, i32, i32, i32]
+        L.mla_lowbit_decode_workspace_bytes.restype = sz
+        L.mla_lowbit_write.argtypes = [P, i32, P, P, P, P, P, P, i32, i32, P, P, P, P]
+        L.mla_lowbit_write.restype = i32
+        L.mla_lowbit_decode.argtypes = [P, i32, i32, ctypes.c_float, P, P, P, P, i32, P, P, P, P, P,
+                                        P, sz, P]
+        L.mla_lowbit_decode.restype = i32
+        L.mla_lowbit_write_decode.argtypes = [P, i32, i32, ctypes.c_float, P, P, P, P, P, P, P, i32,
+                                              P, P, P, P, P, P, sz, P]
+        L.mla_lowbit_write_decode.restype = i32
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    try:
+        return lib().mla_lowbit_strerror(code).decode()
+    except RuntimeError:
+        return f"error {code}"
+
+
+def version() -> int:
+    return lib().mla_lowbit_version()
+
+
+def page_bytes(cfg: Config) -> int:
+    c = cfg.c()
+    return int(lib().mla_lowbit_page_bytes(ctypes.byref(c)))
+
+
+def decode_workspace_bytes(cfg: Config, B: int, H: int, max_pages: int) -> int:
+    c = cfg.c()
+    return int(lib().mla_lowbit_decode_workspace_bytes(ctypes.byref(c), B, H, max_pages))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != OK:
+        raise MlaLowbitError(fn, rc)
+
+
+def _want(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def allocate_cache(cfg: Config, B: int, num_pages: int, device="cuda"):
+    """Zeroed device buffers for a cache: pages uint8 [num_pages, page_bytes],
+    sink / local bf16 [B, n, d_c + d_r]."""
+    D = cfg.d_c + cfg.d_r
+    pages = torch.zeros(num_pages, page_bytes(cfg), dtype=torch.uint8, device=device)
+    sink = torch.zeros(B, max(cfg.n_sink, 1), D, dtype=torch.bfloat16, device=device)
+    local = torch.zeros(B, max(cfg.n_local, 1), D, dtype=torch.bfloat16, device=device)
+    return pages, sink, local
+
+
+def write(cfg: Config, c_kv, k_rope, seq_idx, pos, seq_lens, page_table, pages, sink, local,
+          stream=None) -> None:
+    """mla_lowbit_write: quantize + pack every token, keep BF16 copies of protected ones."""
+    _want(c_kv, torch.bfloat16, "c_kv")
+    _want(k_rope, torch.bfloat16, "k_rope")
+    for n, t in (("seq_idx", seq_idx), ("pos", pos), ("seq_lens", seq_lens),
+                 ("page_table", page_table)):
+        _want(t, torch.int32, n)
+    n = int(seq_idx.numel())
+    if c_kv.shape != (n, cfg.d_c) or k_rope.shape != (n, cfg.d_r) or pos.numel() != n:
+        raise ValueError("c_kv / k_rope / pos do not match seq_idx")
+    B, max_pages = page_table.shape
+    c = cfg.c()
+    rc = lib().mla_lowbit_write(ctypes.byref(c), n, _ptr(c_kv), _ptr(k_rope), _ptr(seq_idx),
+                                _ptr(pos), _ptr(seq_lens), _ptr(page_table), B, max_pages,
+                                _ptr(pages), _ptr(sink), _ptr(local), _stream(stream))
+    _check("mla_lowbit_write", rc)
+
+
+def decode(cfg: Config, q_lat, q_rope, pages, page_table, seq_lens, sink, local, scale: float,
+           out=None, lse=None, workspace=None, stream=None):
+    """mla_lowbit_decode. Returns (out bf16 [B,H,d_c], lse fp32 [B,H])."""
+    _want(q_lat, torch.bfloat16, "q_lat")
+    _want(q_rope, torch.bfloat16, "q_rope")
+    B, H, _ = q_lat.shape
+    max_pages = page_table.shape[1]
+    dev = q_lat.device
+    if out is None:
+        out = torch.empty(B, H, cfg.d_c, dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    need = decode_workspace_bytes(cfg, B, H, max_pages)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    c = cfg.c()
+    rc = lib().mla_lowbit_decode(ctypes.byref(c), B, H, float(scale), _ptr(q_lat), _ptr(q_rope),
+                                 _ptr(pages), _ptr(page_table), max_pages, _ptr(seq_lens),
+                                 _ptr(sink), _ptr(local), _ptr(out), _ptr(lse), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("mla_lowbit_decode", rc)
+    return out, lse
+
+
+def write_decode(cfg: Config, c_kv, k_rope, pos, q_lat, q_rope, pages, page_table, seq_lens,
+                 sink, local, scale: float, out=None, lse=None, workspace=None, stream=None):
+    """mla_lowbit_write_decode: one new token per sequence, then decode."""
+    B, H, _ = q_lat.shape
+    max_pages = page_table.shape[1]
+    dev = q_lat.device
+    if out is None:
+        out = torch.empty(B, H, cfg.d_c, dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    need = decode_workspace_bytes(cfg, B, H, max_pages)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    c = cfg.c()
+    rc = lib().mla_lowbit_write_decode(ctypes.byref(c), B, H, float(scale), _ptr(c_kv),
+                                       _ptr(k_rope), _ptr(pos), _ptr(q_lat), _ptr(q_rope),
+                                       _ptr(pages), _ptr(page_table), max_pages, _ptr(seq_lens),
+                                       _ptr(sink), _ptr(local), _ptr(out), _ptr(lse),
+                                       _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream))
+    _check("mla_lowbit_write_decode", rc)
+    return out, lse

@@ -1,0 +1,198 @@
+// C-ABI entry points (include/mla_lowbit.h): host-side validation, size
+// queries and launches on the caller's stream. Nothing here allocates,
+// synchronizes or keeps state.
+#include <math.h>
+
+#include "../../include/mla_lowbit.h"
+#include "mla_common.h"
+#include "mla_kernels.h"
+
+using namespace mla;
+
+namespace {
+
+int check_cfg(const mla_lowbit_config* c) {
+  if (!c) return MLA_LOWBIT_EINVAL;
+  if (c->d_c != D_C || c->d_r != D_R || c->group != GROUP || c->page_size != PAGE)
+    return MLA_LOWBIT_EUNSUPPORTED;
+  if ((c->c_bits != 4 && c->c_bits != 2) || c->r_bits != 4) return MLA_LOWBIT_EUNSUPPORTED;
+  if (c->n_sink < 0 || c->n_sink > 64 || c->n_local < 0 || c->n_local > 256)
+    return MLA_LOWBIT_EUNSUPPORTED;
+  return MLA_LOWBIT_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+bool ok_ptr4(const void* p) { return p != nullptr && ((uintptr_t)p & 3u) == 0; }
+
+int write_checks(const mla_lowbit_config* cfg, int n_tokens, const void* c_kv,
+                 const void* k_rope, const int32_t* pos, const int32_t* seq_lens,
+                 const int32_t* page_table, int B, int max_pages, void* pages, void* sink,
+                 void* local) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (n_tokens < 0 || B < 0 || max_pages < 1) return MLA_LOWBIT_EINVAL;
+  if (n_tokens == 0) return MLA_LOWBIT_OK;
+  if (B == 0) return MLA_LOWBIT_EINVAL;
+  if (!ok_ptr(c_kv) || !ok_ptr(k_rope) || !ok_ptr4(pos) || !ok_ptr4(seq_lens) ||
+      !ok_ptr4(page_table) || !ok_ptr(pages))
+    return MLA_LOWBIT_EINVAL;
+  if (cfg->n_sink > 0 && !ok_ptr(sink)) return MLA_LOWBIT_EINVAL;
+  if (cfg->n_local > 0 && !ok_ptr(local)) return MLA_LOWBIT_EINVAL;
+  return MLA_LOWBIT_OK;
+}
+
+int decode_checks(const mla_lowbit_config* cfg, int B, int H, float softmax_scale,
+                  const void* q_lat, const void* q_rope, const void* pages,
+                  const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                  const void* sink, const void* local, void* out, float* lse, void* workspace,
+                  size_t workspace_bytes) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (B < 0 || H <= 0 || H % 16 != 0 || max_pages < 1) return MLA_LOWBIT_EINVAL;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_LOWBIT_EINVAL;
+  if (B == 0) return MLA_LOWBIT_OK;
+  if (!ok_ptr(q_lat) || !ok_ptr(q_rope) || !ok_ptr(pages) || !ok_ptr4(page_table) ||
+      !ok_ptr4(seq_lens) || !ok_ptr(out) || !ok_ptr(lse) || !ok_ptr(workspace))
+    return MLA_LOWBIT_EINVAL;
+  if (cfg->n_sink > 0 && !ok_ptr(sink)) return MLA_LOWBIT_EINVAL;
+  if (cfg->n_local > 0 && !ok_ptr(local)) return MLA_LOWBIT_EINVAL;
+  if (workspace_bytes < decode_workspace_bytes(B, H, max_pages)) return MLA_LOWBIT_EWORKSPACE;
+  return MLA_LOWBIT_OK;
+}
+
+DecodeArgs make_decode_args(const mla_lowbit_config* cfg, int B, int H, float softmax_scale,
+                            const void* q_lat, const void* q_rope, const void* pages,
+                            const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                            const void* sink, const void* local, void* out, float* lse,
+                            void* workspace) {
+  const SplitPlan sp = plan_splits(B, H, max_pages);
+  DecodeArgs a;
+  a.q_lat = static_cast<const uint16_t*>(q_lat);
+  a.q_rope = static_cast<const uint16_t*>(q_rope);
+  a.pages = static_cast<const uint8_t*>(pages);
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.seq_lens = seq_lens;
+  a.sink = static_cast<const uint16_t*>(sink);
+  a.local = static_cast<const uint16_t*>(local);
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = a.ws_o + (size_t)B * sp.n_split * H * D_C;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.n_split = sp.n_split;
+  a.pages_per_split = sp.pages_per_split;
+  a.n_sink = cfg->n_sink;
+  a.n_local = cfg->n_local;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_lowbit_version(void) { return 100; }
+
+const char* mla_lowbit_strerror(int code) {
+  switch (code) {
+    case MLA_LOWBIT_OK: return "ok";
+    case MLA_LOWBIT_EINVAL: return "invalid argument (null/misaligned pointer, count or shape)";
+    case MLA_LOWBIT_EUNSUPPORTED: return "unsupported cache configuration";
+    case MLA_LOWBIT_EWORKSPACE: return "workspace smaller than mla_lowbit_decode_workspace_bytes";
+    case MLA_LOWBIT_ELAUNCH: return "HIP kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+int mla_lowbit_check_config(const mla_lowbit_config* cfg) { return check_cfg(cfg); }
+
+size_t mla_lowbit_page_bytes(const mla_lowbit_config* cfg) {
+  if (check_cfg(cfg)) return 0;
+  return cfg->c_bits == 4 ? (size_t)PageGeom<4>::BYTES : (size_t)PageGeom<2>::BYTES;
+}
+
+size_t mla_lowbit_decode_workspace_bytes(const mla_lowbit_config* cfg, int B, int H,
+                                         int max_pages) {
+  if (check_cfg(cfg) || B < 0 || H <= 0 || H % 16 != 0 || max_pages < 1) return 0;
+  return decode_workspace_bytes(B, H, max_pages);
+}
+
+int mla_lowbit_write(const mla_lowbit_config* cfg, int n_tokens, const void* c_kv,
+                     const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                     const int32_t* seq_lens, const int32_t* page_table, int B, int max_pages,
+                     void* pages, void* sink, void* local, void* stream) {
+  int rc = write_checks(cfg, n_tokens, c_kv, k_rope, pos, seq_lens, page_table, B, max_pages,
+                        pages, sink, local);
+  if (rc || n_tokens == 0) return rc;
+  if (!ok_ptr4(seq_idx)) return MLA_LOWBIT_EINVAL;
+  WriteArgs a;
+  a.n_tokens = n_tokens;
+  a.c_kv = static_cast<const uint16_t*>(c_kv);
+  a.k_rope = static_cast<const uint16_t*>(k_rope);
+  a.seq_idx = seq_idx;
+  a.pos = pos;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.pages = static_cast<uint8_t*>(pages);
+  a.sink = static_cast<uint16_t*>(sink);
+  a.local = static_cast<uint16_t*>(local);
+  a.n_sink = cfg->n_sink;
+  a.n_local = cfg->n_local;
+  return launch_write(a, cfg->c_bits, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_LOWBIT_OK
+             : MLA_LOWBIT_ELAUNCH;
+}
+
+int mla_lowbit_decode(const mla_lowbit_config* cfg, int B, int H, float softmax_scale,
+                      const void* q_lat, const void* q_rope, const void* pages,
+                      const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                      const void* sink, const void* local, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = decode_checks(cfg, B, H, softmax_scale, q_lat, q_rope, pages, page_table, max_pages,
+                         seq_lens, sink, local, out, lse, workspace, workspace_bytes);
+  if (rc || B == 0) return rc;
+  DecodeArgs a = make_decode_args(cfg, B, H, softmax_scale, q_lat, q_rope, pages, page_table,
+                                  max_pages, seq_lens, sink, local, out, lse, workspace);
+  return launch_decode(a, cfg->c_bits, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_LOWBIT_OK
+             : MLA_LOWBIT_ELAUNCH;
+}
+
+int mla_lowbit_write_decode(const mla_lowbit_config* cfg, int B, int H, float softmax_scale,
+                            const void* c_kv, const void* k_rope, const int32_t* pos,
+                            const void* q_lat, const void* q_rope, void* pages,
+                            const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                            void* sink, void* local, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  int rc = write_checks(cfg, B, c_kv, k_rope, pos, seq_lens, page_table, B, max_pages, pages,
+                        sink, local);
+  if (rc) return rc;
+  rc = decode_checks(cfg, B, H, softmax_scale, q_lat, q_rope, pages, page_table, max_pages,
+                     seq_lens, sink, local, out, lse, workspace, workspace_bytes);
+  if (rc || B == 0) return rc;
+  WriteArgs w;
+  w.n_tokens = B;
+  w.c_kv = static_cast<const uint16_t*>(c_kv);
+  w.k_rope = static_cast<const uint16_t*>(k_rope);
+  w.seq_idx = nullptr;  // token t belongs to sequence t
+  w.pos = pos;
+  w.seq_lens = seq_lens;
+  w.page_table = page_table;
+  w.max_pages = max_pages;
+  w.pages = static_cast<uint8_t*>(pages);
+  w.sink = static_cast<uint16_t*>(sink);
+  w.local = static_cast<uint16_t*>(local);
+  w.n_sink = cfg->n_sink;
+  w.n_local = cfg->n_local;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_write(w, cfg->c_bits, s) != hipSuccess) return MLA_LOWBIT_ELAUNCH;
+  DecodeArgs a = make_decode_args(cfg, B, H, softmax_scale, q_lat, q_rope, pages, page_table,
+                                  max_pages, seq_lens, sink, local, out, lse, workspace);
+  return launch_decode(a, cfg->c_bits, s) == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ELAUNCH;
+}
+
+}  // extern "C"

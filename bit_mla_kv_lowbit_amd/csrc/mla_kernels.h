@@ -1,0 +1,51 @@
+// Kernel argument blocks and launchers shared by the C-ABI entry points.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct WriteArgs {
+  int n_tokens;
+  const uint16_t* c_kv;     // bf16 [n, 512]
+  const uint16_t* k_rope;   // bf16 [n, 64]
+  const int32_t* seq_idx;   // [n] or null (token t belongs to sequence t)
+  const int32_t* pos;       // [n]
+  const int32_t* seq_lens;  // [B], after the write
+  const int32_t* page_table;
+  int max_pages;
+  uint8_t* pages;
+  uint16_t* sink;
+  uint16_t* local;
+  int n_sink, n_local;
+};
+
+struct DecodeArgs {
+  const uint16_t* q_lat;   // bf16 [B, H, 512]
+  const uint16_t* q_rope;  // bf16 [B, H, 64]
+  const uint8_t* pages;
+  const int32_t* page_table;
+  int max_pages;
+  const int32_t* seq_lens;
+  const uint16_t* sink;
+  const uint16_t* local;
+  float* ws_o;    // [B, n_split, H, 512] fp32 partial outputs (normalized)
+  float* ws_lse;  // [B, n_split, H] fp32 partial log-sum-exp (natural log)
+  uint16_t* out;  // bf16 [B, H, 512]
+  float* lse;     // fp32 [B, H]
+  int B, H, n_split, pages_per_split, n_sink, n_local;
+  float scale_log2;  // softmax_scale * log2(e)
+};
+
+struct SplitPlan {
+  int n_split;
+  int pages_per_split;
+};
+
+SplitPlan plan_splits(int B, int H, int max_pages);
+size_t decode_workspace_bytes(int B, int H, int max_pages);
+
+hipError_t launch_write(const WriteArgs& a, int c_bits, hipStream_t stream);
+hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream);
+
+}  // namespace mla

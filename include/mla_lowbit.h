@@ -1,0 +1,166 @@
+/*
+ * mla_lowbit: packed low-bit MLA KV cache writer and absorbed-MLA decode for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is QuantMLA ("QuantMLA: Function-Aligned Dual-Path Quantization
+ * for Low-Bit MLA KV Caching", newx.sg summary page and thelatestinai.com
+ * cards page):
+ *   - the cache keeps the content latent c_kv and the decoupled RoPE key
+ *     k_rope as low-bit codes: INT4 + INT4 ("C4R4") or INT2 content with an
+ *     INT4 RoPE key ("C2R4") (abstract);
+ *   - a fused writer produces a packed copy of every incoming token and keeps
+ *     the pre-quantization BF16 values of protected sink and recent tokens in
+ *     dedicated buffers (Figure 8 caption; Figure 3 caption);
+ *   - the protection policy is sink4/local128 (Figure 5 and Table 9 captions);
+ *   - attention unpacks and dequantizes inside the kernel, reads BF16 values
+ *     for protected tokens, shares one reconstructed content tile between the
+ *     matching (QK) and aggregation (PV) products, and normalizes all valid
+ *     tokens with one softmax (Figure 8 caption; abstract);
+ *   - decode is the absorbed (MQA) form of MLA: every query head attends over
+ *     the one shared latent (GQLA card on the same cards page).
+ * The pages fix no quantizer formula, code order, page layout or partitioning;
+ * the choices made here are stated below.
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers, owned and allocated by the
+ *     caller, 16-byte aligned. The library never allocates, frees,
+ *     synchronizes or keeps state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
+ *     work on it and return; results are ready when the stream reaches them.
+ *   - bf16 / fp16 arrays hold the raw 16-bit patterns.
+ *   - Return value: MLA_LOWBIT_OK (0) or a negative error code. Arguments are
+ *     validated on the host before anything is launched; on an error nothing
+ *     is enqueued. Contents of device buffers are not validated: an
+ *     out-of-range page-table entry, position or length is undefined behaviour.
+ *   - Calls are reentrant and thread-safe.
+ *
+ * Quantizer (per token, per group of 32 contiguous channels; bit-exact):
+ *   lo = min, hi = max of the group (bf16 values widened to fp32);
+ *   s = fp16_rne(fp32(hi - lo) / fp32(2^b - 1)), z = fp16_rne(lo);
+ *   q = 0 if s == 0, else clamp(rint_even((x - z) / s), 0, 2^b - 1) in fp32;
+ *   the decode reconstructs x = q * s + z.
+ *
+ * Page layout (page_size = 64 token slots; slot = pos % 64 in page
+ * page_table[b][pos / 64]); four token-major regions, C4R4 / C2R4:
+ *   content codes  [64][256 | 128] B   at 0
+ *   RoPE codes     [64][32] B          at 16384 | 8192
+ *   content (s,z)  [64][16][2] fp16    at 18432 | 10240
+ *   RoPE (s,z)     [64][2][2] fp16     at 22528 | 14336
+ *   page bytes     23040 | 14848       (360 | 232 B per token)
+ * Code order: each little-endian 32-bit word holds 32/b consecutive channels;
+ * channel 2a+k of the word (k = 0, 1) sits in code slot a + k * 16/b, i.e.
+ * even channels fill the low half-word and odd channels the high half-word.
+ *
+ * Protected tokens (sink / local buffers, bf16 [B][n][d_c + d_r], row =
+ * [c_kv | k_rope]): token p of a sequence of length L is read from
+ * sink[b][p] if p < n_sink, else from local[b][p % n_local] if
+ * p >= L - n_local, else from its packed copy.
+ */
+#ifndef MLA_LOWBIT_H
+#define MLA_LOWBIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_LOWBIT_OK 0
+#define MLA_LOWBIT_EINVAL (-1)       /* null/misaligned pointer, bad count or shape */
+#define MLA_LOWBIT_EUNSUPPORTED (-2) /* configuration outside what the kernels build */
+#define MLA_LOWBIT_EWORKSPACE (-3)   /* workspace smaller than the size query says */
+#define MLA_LOWBIT_ELAUNCH (-4)      /* the HIP runtime reported a launch error */
+
+/* Cache geometry. Supported: d_c = 512, d_r = 64, c_bits in {4, 2}, r_bits = 4,
+ * group = 32, page_size = 64, 0 <= n_sink <= 64, 0 <= n_local <= 256. */
+typedef struct mla_lowbit_config {
+  int32_t d_c;       /* content latent width */
+  int32_t d_r;       /* decoupled RoPE key width */
+  int32_t c_bits;    /* content code bits */
+  int32_t r_bits;    /* RoPE key code bits */
+  int32_t group;     /* channels per (scale, zero) group */
+  int32_t page_size; /* token slots per page */
+  int32_t n_sink;    /* leading tokens kept in BF16 */
+  int32_t n_local;   /* most recent tokens kept in BF16 (ring of n_local slots) */
+} mla_lowbit_config;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int mla_lowbit_version(void);
+
+/* Static message for an error code (never NULL). */
+const char* mla_lowbit_strerror(int code);
+
+/* MLA_LOWBIT_OK if the kernels support `cfg`, else EINVAL / EUNSUPPORTED. */
+int mla_lowbit_check_config(const mla_lowbit_config* cfg);
+
+/* Bytes of one cache page (23040 for C4R4, 14848 for C2R4); 0 if unsupported. */
+size_t mla_lowbit_page_bytes(const mla_lowbit_config* cfg);
+
+/* Workspace bytes mla_lowbit_decode needs for this shape (depends only on
+ * host-side scalars); 0 if unsupported. */
+size_t mla_lowbit_decode_workspace_bytes(const mla_lowbit_config* cfg, int B, int H,
+                                         int max_pages);
+
+/*
+ * Fused writer (Figure 8 caption: a packed copy for every incoming token, plus
+ * the pre-quantization BF16 values of protected tokens).
+ *   n_tokens    tokens to write (>= 0; 0 is a no-op)
+ *   c_kv        bf16 [n_tokens, d_c]   content latents
+ *   k_rope      bf16 [n_tokens, d_r]   RoPE keys, already rotated
+ *   seq_idx     int32 [n_tokens]       sequence of each token, in [0, B)
+ *   pos         int32 [n_tokens]       position of each token in its sequence
+ *   seq_lens    int32 [B]              sequence lengths AFTER this write
+ *   page_table  int32 [B, max_pages]   physical page of each logical page
+ *   pages       uint8 [num_pages, page_bytes]   packed cache (written)
+ *   sink        bf16 [B, n_sink, d_c + d_r]     (written for pos < n_sink)
+ *   local       bf16 [B, n_local, d_c + d_r]    (written for pos >= len - n_local)
+ * Each (seq, pos) may appear at most once per call, so no ring slot is
+ * written twice by one call. A token leaving the recent window needs no
+ * call: its packed copy already exists (Figure 8 caption).
+ */
+int mla_lowbit_write(const mla_lowbit_config* cfg, int n_tokens, const void* c_kv,
+                     const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                     const int32_t* seq_lens, const int32_t* page_table, int B, int max_pages,
+                     void* pages, void* sink, void* local, void* stream);
+
+/*
+ * Absorbed-MLA decode over the mixed BF16 / packed cache (abstract; Figure 8
+ * caption; GQLA card). For every sequence b and head h, over tokens
+ * p < seq_lens[b]:
+ *   score[p] = softmax_scale * (q_lat[b,h] . c[p] + q_rope[b,h] . k_rope[p])
+ *   out[b,h] = sum_p softmax(score)[p] * c[p]          (bf16, RNE)
+ *   lse[b,h] = log(sum_p exp(score[p]))                (fp32, natural log)
+ * with c / k_rope read from BF16 buffers for protected tokens and
+ * dequantized otherwise. A sequence of length 0 gives out = 0, lse = -inf.
+ *   H            heads, a positive multiple of 16
+ *   q_lat        bf16 [B, H, d_c];  q_rope  bf16 [B, H, d_r]
+ *   out          bf16 [B, H, d_c];  lse     fp32 [B, H]
+ *   workspace    device scratch of at least
+ *                mla_lowbit_decode_workspace_bytes(cfg, B, H, max_pages) bytes
+ * The sequence is split into page ranges processed in parallel and merged by
+ * their log-sum-exp (one global softmax, Figure 8 caption).
+ */
+int mla_lowbit_decode(const mla_lowbit_config* cfg, int B, int H, float softmax_scale,
+                      const void* q_lat, const void* q_rope, const void* pages,
+                      const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                      const void* sink, const void* local, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One serving step (Figure 8 caption): write one new token per sequence
+ * (mla_lowbit_write with n_tokens = B, seq_idx = 0..B-1, pos[b] =
+ * seq_lens[b] - 1), then decode every sequence including its new token.
+ * Arguments as in the two calls above; enqueued in that order on `stream`.
+ */
+int mla_lowbit_write_decode(const mla_lowbit_config* cfg, int B, int H, float softmax_scale,
+                            const void* c_kv, const void* k_rope, const int32_t* pos,
+                            const void* q_lat, const void* q_rope, void* pages,
+                            const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                            void* sink, void* local, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

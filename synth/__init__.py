@@ -162,8 +162,10 @@ def sequence_tokens(b: int, start: int, stop: int, seed: int, device="cpu", d_c:
 
 
 def build_cache_inputs(lens: List[int], H: int, seed: int, device="cpu", d_c: int = D_C,
-                       d_r: int = D_R, page: int = PAGE, outliers=True, spare_pages: int = 0):
-    """All tokens 0..L_b-1 of every sequence, in sequence order, plus queries."""
+                       d_r: int = D_R, page: int = PAGE, outliers=True, spare_pages: int = 0,
+                       table_lens: Optional[List[int]] = None):
+    """All tokens 0..L_b-1 of every sequence, in sequence order, plus queries.
+    The page table covers table_lens (default: lens) tokens per sequence."""
     outl = outlier_channels(seed, d_c) if outliers else None
     cs, rs, si, ps = [], [], [], []
     for b, L in enumerate(lens):
@@ -174,7 +176,8 @@ def build_cache_inputs(lens: List[int], H: int, seed: int, device="cpu", d_c: in
         rs.append(r)
         si.append(torch.full((L,), b, dtype=torch.int32, device=device))
         ps.append(torch.arange(L, dtype=torch.int32, device=device))
-    pt, total = page_table(lens, seed, page, spare_pages)
+    pt, total = page_table(table_lens if table_lens is not None else lens, seed, page,
+                           spare_pages)
     q_lat, q_rope = queries(len(lens), H, seed + 99, device, d_c, d_r)
     empty_c = torch.zeros(0, d_c, dtype=torch.bfloat16, device=device)
     empty_r = torch.zeros(0, d_r, dtype=torch.bfloat16, device=device)
@@ -190,3 +193,32 @@ def build_cache_inputs(lens: List[int], H: int, seed: int, device="cpu", d_c: in
         q_lat=q_lat,
         q_rope=q_rope,
     )
+
+
+@dataclass
+class StepTokens:
+    """One new token per sequence for a serving step (written at position pos[b])."""
+    c_kv: torch.Tensor    # [B, d_c] bf16
+    k_rope: torch.Tensor  # [B, d_r] bf16
+    pos: torch.Tensor     # [B] int32
+    seq_lens: torch.Tensor  # [B] int32, lengths after the step
+
+
+def workload_inputs(wl: Workload, device="cpu"):
+    """Bulk cache contents of a workload (tokens present before the step) and, for
+    a serving step, the new tokens. Returns (CacheInputs, StepTokens or None)."""
+    lens = wl.lengths()
+    if not wl.step_write:
+        return build_cache_inputs(lens, wl.H, wl.seed, device), None
+    pre = [L - 1 for L in lens]
+    inp = build_cache_inputs(pre, wl.H, wl.seed, device, table_lens=lens)
+    outl = outlier_channels(wl.seed)
+    cs, rs = [], []
+    for b, p in enumerate(pre):
+        c, r = sequence_tokens(b, p, p + 1, wl.seed, device, outliers=outl)
+        cs.append(c)
+        rs.append(r)
+    step = StepTokens(torch.cat(cs), torch.cat(rs),
+                      torch.tensor(pre, dtype=torch.int32, device=device),
+                      torch.tensor(lens, dtype=torch.int32, device=device))
+    return inp, step

@@ -14,12 +14,14 @@ def cfg_for(c_bits: int = 4, **kw) -> oracle.Cfg:
     return oracle.Cfg(c_bits=c_bits, **kw)
 
 
-def oracle_cache(cfg: oracle.Cfg, inp, B: int):
-    """Run the oracle writer over every token of `inp` into fresh host buffers."""
+def oracle_cache(cfg: oracle.Cfg, inp, B: int, canary=None):
+    """Run the oracle writer over every token of `inp` into fresh host buffers
+    (zeroed, or filled with a canary byte)."""
     D = cfg.d_c + cfg.d_r
-    pages = np.zeros((inp.num_pages, oracle.page_bytes(cfg)), np.uint8)
-    sink = np.zeros((B, max(cfg.n_sink, 1), D), np.uint16)
-    local = np.zeros((B, max(cfg.n_local, 1), D), np.uint16)
+    fill = 0 if canary is None else canary
+    pages = np.full((inp.num_pages, oracle.page_bytes(cfg)), fill, np.uint8)
+    sink = np.full((B, max(cfg.n_sink, 1), D), fill * 257, np.uint16)
+    local = np.full((B, max(cfg.n_local, 1), D), fill * 257, np.uint16)
     oracle.write(cfg, u16(inp.c_kv), u16(inp.k_rope), inp.seq_idx.cpu().numpy(),
                  inp.pos.cpu().numpy(), inp.seq_lens.cpu().numpy(),
                  inp.page_table.cpu().numpy(), pages, sink, local)

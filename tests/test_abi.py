@@ -1,0 +1,110 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol that
+include/mla_lowbit.h declares, answers the size queries, and rejects bad
+arguments on the host before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_mla_kv_lowbit_amd as mla
+from bit_mla_kv_lowbit_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_lowbit.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_lowbit_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ["mla_lowbit_write", "mla_lowbit_decode", "mla_lowbit_write_decode",
+              "mla_lowbit_page_bytes", "mla_lowbit_decode_workspace_bytes",
+              "mla_lowbit_strerror", "mla_lowbit_version", "mla_lowbit_check_config"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(binding.LIB_PATH)
+    for n in _declared():
+        assert hasattr(L, n), n
+
+
+def test_size_queries():
+    assert mla.page_bytes(mla.C4R4) == 23040
+    assert mla.page_bytes(mla.C2R4) == 14848
+    assert mla.page_bytes(mla.Config(group=64)) == 0
+    ws = mla.decode_workspace_bytes(mla.C4R4, 8, 16, 512)
+    assert ws > 0 and ws % 4 == 0
+    assert mla.decode_workspace_bytes(mla.C4R4, 8, 24, 512) == 0  # H not a multiple of 16
+    assert mla.decode_workspace_bytes(mla.C4R4, 8, 16, 0) == 0
+    assert mla.version() >= 100
+    assert "workspace" in binding.strerror(binding.EWORKSPACE)
+
+
+@pytest.mark.parametrize("bad", [dict(d_c=256), dict(d_r=32), dict(c_bits=3), dict(r_bits=2),
+                                 dict(group=16), dict(page_size=32), dict(n_sink=65),
+                                 dict(n_local=257), dict(n_sink=-1)])
+def test_unsupported_configs(bad):
+    c = mla.Config(**bad).c()
+    assert mla.lib().mla_lowbit_check_config(ctypes.byref(c)) == binding.EUNSUPPORTED
+
+
+def _fake(addr=0x10000):
+    return ctypes.c_void_p(addr)
+
+
+def _decode_call(cfg=mla.C4R4, B=2, H=16, scale=0.1, ws_bytes=1 << 40, **over):
+    args = dict(q_lat=_fake(), q_rope=_fake(), pages=_fake(), page_table=_fake(),
+                seq_lens=_fake(), sink=_fake(), local=_fake(), out=_fake(), lse=_fake(),
+                ws=_fake())
+    args.update(over)
+    c = cfg.c()
+    return mla.lib().mla_lowbit_decode(ctypes.byref(c), B, H, scale, args["q_lat"],
+                                       args["q_rope"], args["pages"], args["page_table"], 4,
+                                       args["seq_lens"], args["sink"], args["local"], args["out"],
+                                       args["lse"], args["ws"], ws_bytes, None)
+
+
+def test_decode_validation_errors():
+    # each call fails host-side validation, so nothing is launched
+    assert _decode_call(H=24) == binding.EINVAL
+    assert _decode_call(H=0) == binding.EINVAL
+    assert _decode_call(B=-1) == binding.EINVAL
+    assert _decode_call(scale=0.0) == binding.EINVAL
+    assert _decode_call(scale=float("nan")) == binding.EINVAL
+    assert _decode_call(q_lat=None) == binding.EINVAL
+    assert _decode_call(out=_fake(0x10008)) == binding.EINVAL  # misaligned
+    assert _decode_call(ws_bytes=16) == binding.EWORKSPACE
+    assert _decode_call(cfg=mla.Config(c_bits=3)) == binding.EUNSUPPORTED
+    # zero sequences is a valid no-op
+    assert _decode_call(B=0) == binding.OK
+
+
+def test_write_validation_errors():
+    c = mla.C4R4.c()
+    L = mla.lib()
+
+    def call(n=4, B=2, max_pages=4, c_kv=_fake(), pages=_fake(), sink=_fake(), cfg=c):
+        return L.mla_lowbit_write(ctypes.byref(cfg), n, c_kv, _fake(), _fake(), _fake(), _fake(),
+                                  _fake(), B, max_pages, pages, sink, _fake(), None)
+
+    assert call(n=-1) == binding.EINVAL
+    assert call(c_kv=None) == binding.EINVAL
+    assert call(pages=_fake(0x10004)) == binding.EINVAL
+    assert call(sink=None) == binding.EINVAL
+    assert call(max_pages=0) == binding.EINVAL
+    assert call(B=0) == binding.EINVAL
+    assert call(cfg=mla.Config(r_bits=2).c()) == binding.EUNSUPPORTED
+    assert call(n=0) == binding.OK  # nothing to write
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    t = torch.zeros(4, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding._ptr(t)

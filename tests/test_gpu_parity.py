@@ -1,0 +1,216 @@
+"""GPU parity: the HIP writer and decode (called through the C ABI) against the
+CPU oracle on the same seeded inputs.
+
+* writer: packed pages, sink and local buffers bit-exact (canary-filled
+  buffers, so bytes outside written slots must keep their canary value);
+* decode: rel-L2 <= 2e-3, |delta| / max(1, |ref|) <= 1e-2 and lse |delta| <= 1e-3
+  against the fp64 oracle, on edge lengths (all-protected, window edges, ragged
+  last pages, empty sequences), both code widths and H in {16, 128}; at the
+  full workload sizes on sampled (sequence, head) rows in the same launch
+  configuration the bench times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_mla_kv_lowbit_amd as mla
+import oracle
+import synth
+from tests.gpu_helpers import (DEV, assert_decode_ok, gpu_cache, gpu_decode, ocfg_of, u16)
+from tests.oracle_helpers import oracle_cache, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+EDGE_LENS = [1, 3, 4, 5, 63, 64, 65, 131, 132, 133, 195, 196, 197, 1000, 0]
+
+
+def _cfg(c_bits):
+    return mla.Config(c_bits=c_bits)
+
+
+@pytest.mark.parametrize("c_bits", [4, 2])
+def test_writer_bit_exact_with_canaries(c_bits):
+    cfg = _cfg(c_bits)
+    lens = [1024, 1, 3, 4, 5, 63, 64, 65, 131, 132, 133, 197, 300]
+    inp = synth.build_cache_inputs(lens, 16, seed=77 + c_bits, device="cpu", spare_pages=3)
+    print(f"[case] writer c_bits={c_bits} lens={lens}", flush=True)
+    pages, sink, local = gpu_cache(cfg, inp, len(lens), canary=0xA5)
+    torch.cuda.synchronize()
+    op, osink, olocal = oracle_cache(ocfg_of(cfg), inp, len(lens), canary=0xA5)
+    assert np.array_equal(pages.cpu().numpy(), op)
+    assert np.array_equal(u16(sink), osink)
+    assert np.array_equal(u16(local), olocal)
+
+
+def test_writer_degenerate_groups():
+    """Constant groups, exact zeros and tiny ranges whose fp16 scale underflows."""
+    cfg = _cfg(4)
+    inp = synth.build_cache_inputs([200], 16, seed=5, device="cpu")
+    c = inp.c_kv.float()
+    c[0:50, 0:32] = 1.5                       # constant group
+    c[50:60, 32:64] = 0.0                     # all-zero group
+    c[60:70, 64:96] = 1.0
+    c[60:70, 64] = 1.0078125                  # range 2^-7 / 15 is still normal fp16
+    c[70:80, 96:128] = 1e-4 * torch.randn(10, 32)  # fp16-subnormal scales
+    c[80:90, 128:160] = -0.0
+    inp.c_kv = c.to(torch.bfloat16)
+    print("[case] writer degenerate groups", flush=True)
+    pages, sink, local = gpu_cache(cfg, inp, 1)
+    torch.cuda.synchronize()
+    op, osink, olocal = oracle_cache(ocfg_of(cfg), inp, 1)
+    assert np.array_equal(pages.cpu().numpy(), op)
+    assert np.array_equal(u16(local), olocal)
+
+
+@pytest.mark.parametrize("c_bits", [4, 2])
+@pytest.mark.parametrize("H", [16, 128])
+def test_decode_edge_lengths(c_bits, H):
+    cfg = _cfg(c_bits)
+    inp = synth.build_cache_inputs(EDGE_LENS, H, seed=300 + H + c_bits, device="cpu")
+    print(f"[case] decode edges c_bits={c_bits} H={H}", flush=True)
+    pages, sink, local = gpu_cache(cfg, inp, len(EDGE_LENS))
+    out, lse = gpu_decode(cfg, inp, pages, sink, local)
+    torch.cuda.synchronize()
+    oc = ocfg_of(cfg)
+    op, osink, olocal = oracle_cache(oc, inp, len(EDGE_LENS))
+    ref, ref_lse = oracle_decode(oc, inp, op, osink, olocal, synth.SOFTMAX_SCALE)
+    assert_decode_ok(out, lse, ref, ref_lse, label=f"edges c{c_bits} H{H}")
+    # the empty sequence gives zeros and -inf
+    b0 = EDGE_LENS.index(0)
+    assert not out[b0].float().abs().sum().item()
+    assert torch.isneginf(lse[b0]).all()
+
+
+def test_decode_tiny_workload():
+    wl = synth.WORKLOADS["tiny"]
+    cfg = _cfg(wl.c_bits)
+    inp, _ = synth.workload_inputs(wl, device="cpu")
+    print("[case] tiny workload", flush=True)
+    pages, sink, local = gpu_cache(cfg, inp, wl.B)
+    out, lse = gpu_decode(cfg, inp, pages, sink, local)
+    torch.cuda.synchronize()
+    oc = ocfg_of(cfg)
+    op, osink, olocal = oracle_cache(oc, inp, wl.B)
+    assert np.array_equal(pages.cpu().numpy(), op)
+    ref, ref_lse = oracle_decode(oc, inp, op, osink, olocal, synth.SOFTMAX_SCALE)
+    assert_decode_ok(out, lse, ref, ref_lse, label="tiny")
+
+
+def test_decode_deterministic():
+    cfg = _cfg(4)
+    inp = synth.build_cache_inputs([3000, 700], 16, seed=9, device="cpu")
+    pages, sink, local = gpu_cache(cfg, inp, 2)
+    o1, l1 = gpu_decode(cfg, inp, pages, sink, local)
+    o2, l2 = gpu_decode(cfg, inp, pages, sink, local)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_serving_steps_across_the_window_edge():
+    """Fused write+decode steps one token at a time as the sequences cross the
+    sink/local boundaries; each step equals a from-scratch oracle build."""
+    cfg = _cfg(4)
+    oc = ocfg_of(cfg)
+    H = 16
+    start = [120, 1, 60]
+    n_steps = 16
+    final = [s + n_steps for s in start]
+    full = synth.build_cache_inputs(final, H, seed=41, device="cpu")
+    B = len(start)
+    pages, sink, local = mla.allocate_cache(cfg, B, full.num_pages, DEV)
+    # bulk-write the first `start[b]` tokens
+    keep = torch.cat([torch.arange(s) + sum(final[:b]) for b, s in enumerate(start)])
+    pt = full.page_table.to(DEV)
+    mla.write(cfg, full.c_kv[keep].to(DEV), full.k_rope[keep].to(DEV),
+              full.seq_idx[keep].to(DEV), full.pos[keep].to(DEV),
+              torch.tensor(start, dtype=torch.int32, device=DEV), pt, pages, sink, local)
+    q_lat, q_rope = full.q_lat.to(DEV), full.q_rope.to(DEV)
+    for k in range(n_steps):
+        L = [s + k + 1 for s in start]
+        idx = torch.tensor([sum(final[:b]) + s + k for b, s in enumerate(start)])
+        seq_lens = torch.tensor(L, dtype=torch.int32)
+        out, lse = mla.write_decode(cfg, full.c_kv[idx].to(DEV), full.k_rope[idx].to(DEV),
+                                    (seq_lens - 1).to(DEV), q_lat, q_rope, pages, pt,
+                                    seq_lens.to(DEV), sink, local, synth.SOFTMAX_SCALE)
+        torch.cuda.synchronize()
+        # from-scratch oracle at these lengths
+        sel = torch.cat([torch.arange(l) + sum(final[:b]) for b, l in enumerate(L)])
+        sub = synth.CacheInputs(full.c_kv[sel], full.k_rope[sel], full.seq_idx[sel],
+                                full.pos[sel], seq_lens, full.page_table, full.num_pages,
+                                full.q_lat, full.q_rope)
+        op, osink, olocal = oracle_cache(oc, sub, B)
+        ref, ref_lse = oracle_decode(oc, sub, op, osink, olocal, synth.SOFTMAX_SCALE)
+        assert_decode_ok(out, lse, ref, ref_lse, label=f"step {k} L={L}")
+        # every packed copy written so far is bit-exact (window exits re-quantize nothing)
+        assert np.array_equal(pages.cpu().numpy(), op)
+
+
+def _full_workload(name, n_seq, n_head, seed_rows=0):
+    wl = synth.WORKLOADS[name]
+    cfg = _cfg(wl.c_bits)
+    oc = ocfg_of(cfg)
+    print(f"[case] full workload {name}: generating on the GPU", flush=True)
+    inp, step = synth.workload_inputs(wl, device=DEV)
+    pages, sink, local = mla.allocate_cache(cfg, wl.B, inp.num_pages, DEV)
+    pre_lens = inp.seq_lens
+    mla.write(cfg, inp.c_kv, inp.k_rope, inp.seq_idx, inp.pos, pre_lens, inp.page_table, pages,
+              sink, local)
+    if step is None:
+        out, lse = mla.decode(cfg, inp.q_lat, inp.q_rope, pages, inp.page_table, pre_lens, sink,
+                              local, synth.SOFTMAX_SCALE)
+        lens = pre_lens
+    else:
+        out, lse = mla.write_decode(cfg, step.c_kv, step.k_rope, step.pos, inp.q_lat, inp.q_rope,
+                                    pages, inp.page_table, step.seq_lens, sink, local,
+                                    synth.SOFTMAX_SCALE)
+        lens = step.seq_lens
+    torch.cuda.synchronize()
+    print(f"[case] full workload {name}: GPU done, oracle on sampled rows", flush=True)
+    # sampled sequences: shortest, longest and random others
+    lens_h = lens.cpu().numpy()
+    rng = np.random.default_rng(seed_rows)
+    seqs = {int(np.argmin(lens_h)), int(np.argmax(lens_h))}
+    while len(seqs) < min(n_seq, wl.B):
+        seqs.add(int(rng.integers(0, wl.B)))
+    seqs = sorted(seqs)
+    rows = [(b, int(h)) for b in seqs for h in sorted(rng.choice(wl.H, n_head, replace=False))]
+    # oracle cache for the sampled sequences only (same page ids)
+    mask = torch.zeros(inp.seq_idx.numel(), dtype=torch.bool, device=DEV)
+    for b in seqs:
+        mask |= inp.seq_idx == b
+    sub = synth.CacheInputs(inp.c_kv[mask].cpu(), inp.k_rope[mask].cpu(), inp.seq_idx[mask].cpu(),
+                            inp.pos[mask].cpu(), pre_lens.cpu(), inp.page_table.cpu(),
+                            inp.num_pages, inp.q_lat.cpu(), inp.q_rope.cpu())
+    op, osink, olocal = oracle_cache(oc, sub, wl.B)
+    if step is not None:
+        sb = np.array(seqs, np.int32)
+        oracle.write(oc, u16(step.c_kv[seqs]), u16(step.k_rope[seqs]), sb,
+                     step.pos.cpu().numpy()[sb], step.seq_lens.cpu().numpy(),
+                     inp.page_table.cpu().numpy(), op, osink, olocal)
+    ref, ref_lse = oracle.decode(oc, synth.SOFTMAX_SCALE, u16(inp.q_lat), u16(inp.q_rope), op,
+                                 inp.page_table.cpu().numpy(), lens_h, osink, olocal, sel=rows)
+    assert_decode_ok(out, lse, ref, ref_lse, rows=rows, label=f"{name} rows={len(rows)}")
+    # the sampled sequences' pages and BF16 buffers are bit-exact
+    pt = inp.page_table.cpu().numpy()
+    for b in seqs:
+        ids = pt[b, :(int(lens_h[b]) + 63) // 64]
+        assert np.array_equal(pages[torch.from_numpy(ids).long().to(DEV)].cpu().numpy(), op[ids])
+        assert np.array_equal(u16(sink[b]), osink[b])
+        assert np.array_equal(u16(local[b]), olocal[b])
+
+
+def test_full_v2lite_sampled():
+    _full_workload("v2lite", n_seq=3, n_head=16)
+
+
+def test_full_v3_sampled():
+    _full_workload("v3", n_seq=4, n_head=6)
+
+
+def test_full_c2r4_sampled():
+    _full_workload("c2r4", n_seq=2, n_head=4)
+
+
+def test_full_serve_sampled():
+    _full_workload("serve", n_seq=4, n_head=4)
