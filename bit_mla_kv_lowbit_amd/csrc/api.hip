@@ -57,6 +57,7 @@ int decode_checks(const mla_lowbit_config* cfg, int B, int H, float softmax_scal
     return MLA_LOWBIT_EINVAL;
   if (cfg->n_sink > 0 && !ok_ptr(sink)) return MLA_LOWBIT_EINVAL;
   if (cfg->n_local > 0 && !ok_ptr(local)) return MLA_LOWBIT_EINVAL;
+  if (plan_splits(B, H, max_pages).n_split > MAX_SPLITS) return MLA_LOWBIT_EUNSUPPORTED;
   if (workspace_bytes < decode_workspace_bytes(B, H, max_pages)) return MLA_LOWBIT_EWORKSPACE;
   return MLA_LOWBIT_OK;
 }
@@ -136,6 +137,7 @@ int mla_lowbit_write(const mla_lowbit_config* cfg, int n_tokens, const void* c_k
   a.pos = pos;
   a.seq_lens = seq_lens;
   a.page_table = page_table;
+  a.B = B;
   a.max_pages = max_pages;
   a.pages = static_cast<uint8_t*>(pages);
   a.sink = static_cast<uint16_t*>(sink);
@@ -182,6 +184,7 @@ int mla_lowbit_write_decode(const mla_lowbit_config* cfg, int B, int H, float so
   w.pos = pos;
   w.seq_lens = seq_lens;
   w.page_table = page_table;
+  w.B = B;
   w.max_pages = max_pages;
   w.pages = static_cast<uint8_t*>(pages);
   w.sink = static_cast<uint16_t*>(sink);

@@ -13,7 +13,7 @@ struct WriteArgs {
   const int32_t* pos;       // [n]
   const int32_t* seq_lens;  // [B], after the write
   const int32_t* page_table;
-  int max_pages;
+  int B, max_pages;
   uint8_t* pages;
   uint16_t* sink;
   uint16_t* local;
@@ -36,6 +36,11 @@ struct DecodeArgs {
   int B, H, n_split, pages_per_split, n_sink, n_local;
   float scale_log2;  // softmax_scale * log2(e)
 };
+
+// Upper bound on partials per sequence that the combine kernel merges.
+constexpr int MAX_SPLITS = 2048;
+// Upper bound on work items (pages or protected-token chunks) per workgroup.
+constexpr int MAX_ITEMS = 128;
 
 struct SplitPlan {
   int n_split;

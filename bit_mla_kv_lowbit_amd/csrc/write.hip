@@ -22,6 +22,9 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
   const int g = (int)(gid % (NG_C + NG_R));
   const int b = a.seq_idx ? a.seq_idx[t] : t;
   const int p = a.pos[t];
+  // tokens outside the page table (or of no sequence) are dropped, never
+  // written out of bounds
+  if (b < 0 || b >= a.B || p < 0 || p >= a.max_pages * PAGE) return;
   const int L = a.seq_lens[b];
   const int64_t page = a.page_table[(int64_t)b * a.max_pages + p / PAGE];
   const int slot = p % PAGE;

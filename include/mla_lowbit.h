@@ -116,7 +116,9 @@ size_t mla_lowbit_decode_workspace_bytes(const mla_lowbit_config* cfg, int B, in
  *   sink        bf16 [B, n_sink, d_c + d_r]     (written for pos < n_sink)
  *   local       bf16 [B, n_local, d_c + d_r]    (written for pos >= len - n_local)
  * Each (seq, pos) may appear at most once per call, so no ring slot is
- * written twice by one call. A token leaving the recent window needs no
+ * written twice by one call. A token whose seq_idx is outside [0, B) or whose
+ * pos is outside [0, max_pages * page_size) is dropped (nothing is written);
+ * page_table entries must name pages that exist (not checked on the device). A token leaving the recent window needs no
  * call: its packed copy already exists (Figure 8 caption).
  */
 int mla_lowbit_write(const mla_lowbit_config* cfg, int n_tokens, const void* c_kv,
@@ -132,7 +134,8 @@ int mla_lowbit_write(const mla_lowbit_config* cfg, int n_tokens, const void* c_k
  *   out[b,h] = sum_p softmax(score)[p] * c[p]          (bf16, RNE)
  *   lse[b,h] = log(sum_p exp(score[p]))                (fp32, natural log)
  * with c / k_rope read from BF16 buffers for protected tokens and
- * dequantized otherwise. A sequence of length 0 gives out = 0, lse = -inf.
+ * dequantized otherwise. A sequence of length 0 gives out = 0, lse = -inf;
+ * seq_lens[b] is clamped to [0, max_pages * page_size].
  *   H            heads, a positive multiple of 16
  *   q_lat        bf16 [B, H, d_c];  q_rope  bf16 [B, H, d_r]
  *   out          bf16 [B, H, d_c];  lse     fp32 [B, H]
