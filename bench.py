@@ -3,10 +3,12 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v2lite] [--no-cpu]
 
 A step is one mla_lowbit_decode over one batch of the workload (for the serving
-workload: one mla_lowbit_write_decode). Inputs are resident in HBM when timing
-starts. The step rotates over R independent copies of the cache (R * cache
-bytes > 256 MB Infinity Cache), so every step streams its cache from HBM
-rather than from the last step's cache lines.
+workload: one mla_lowbit_write_decode). The W warmup steps and the K timed
+steps are each captured as one HIP graph; the timed region is one replay of
+the K-step graph (--eager launches every step from Python instead). Inputs are
+resident in HBM when timing starts. Step k uses cache copy k mod R, with R
+copies covering more than twice the 256 MB Infinity Cache, so every step
+streams its cache from HBM rather than from the previous step's cache lines.
 
 Prints one JSON line: value = cache tokens attended per second (sum of sequence
 lengths / step time), plus the roofline of the decode call (HIP events on the
@@ -48,6 +50,45 @@ def algorithmic_flops(lens, H):
     return 2 * (576 + 512) * H * sum(lens)
 
 
+DECODE_SOURCES = ("bit_mla_kv_lowbit_amd/csrc/decode.hip", "bit_mla_kv_lowbit_amd/csrc/mla_common.h",
+                  "bit_mla_kv_lowbit_amd/csrc/mla_kernels.h")
+
+
+def decode_source_hash() -> str:
+    """Hash of the decode kernels' sources: HBM traffic counters taken on other
+    sources no longer describe the kernel and are not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary of this workload, or None when it is missing or was taken
+    on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != decode_source_hash():
+        return None
+    try:
+        return {"bytes_per_call": int(float(kv["traffic_bytes_per_call"])),
+                "fetch_bytes": int(float(kv["fetch_bytes_per_call"])),
+                "write_bytes": int(float(kv["write_bytes_per_call"])),
+                "copy_calibration": float(kv["fetch_scale"])}
+    except (KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -55,10 +96,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="v2lite")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from Python instead of replaying HIP graphs")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one elementwise copy of this many MiB (fp32 negation), the "
+                         "known-size kernel that scales the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU sharding is "
+                                   "not implemented, so --gpus must be 1"}))
         sys.exit(2)
 
     import numpy as np
@@ -68,6 +115,16 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 18  # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + "
+              f"{args.calib_copy_mib} MiB written", file=sys.stderr, flush=True)
+
     wl = synth.WORKLOADS[args.workload]
     cfg = mla.Config(c_bits=wl.c_bits)
     print(f"[bench] generating {wl.desc} on the GPU", file=sys.stderr, flush=True)
@@ -87,11 +144,10 @@ def main():
                      dtype=torch.uint8, device=dev)
     out = torch.empty(wl.B, wl.H, 512, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(wl.B, wl.H, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
     seq_lens_dev = step.seq_lens if step is not None else inp.seq_lens
 
-    def one_step(k):
-        p, s, l = reps[k % R]
+    def launch(r, stream):
+        p, s, l = reps[r]
         if step is None:
             mla.decode(cfg, inp.q_lat, inp.q_rope, p, inp.page_table, seq_lens_dev, s, l,
                        synth.SOFTMAX_SCALE, out=out, lse=lse, workspace=ws, stream=stream)
@@ -102,27 +158,68 @@ def main():
 
     print(f"[bench] cache {cache_bytes / 1e6:.1f} MB x {R} copies; warmup {args.warmup}",
           file=sys.stderr, flush=True)
-    for k in range(args.warmup):
-        one_step(k)
+    cur = torch.cuda.current_stream()
+    launch(0, cur)
     torch.cuda.synchronize()
+    eager_out, eager_lse = out.clone(), lse.clone()
 
-    # timed region: exactly K steps; HIP events on the launch stream bracket each call
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        evs[k][0].record(stream)
-        one_step(args.warmup + k)
-        evs[k][1].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if args.eager:
+        for k in range(args.warmup):
+            launch(k % R, cur)
+        # timed region: exactly K steps, each bracketed by HIP events on the launch stream
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            evs[k][0].record(cur)
+            launch((args.warmup + k) % R, cur)
+            evs[k][1].record(cur)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ev_ms = [a.elapsed_time(b) for a, b in evs]
+    else:
+        # the W warmup steps and the K timed steps are each captured in one HIP
+        # graph (step k decodes cache copy k mod R); the timed region is one
+        # replay, bracketed by HIP events on the stream it runs on
+        cap = torch.cuda.Stream()
+        cap.wait_stream(cur)
+
+        def capture(first, n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for k in range(first, first + n):
+                    launch(k % R, torch.cuda.current_stream())
+            return g
+
+        g_warm = capture(0, max(1, args.warmup))
+        g_timed = capture(args.warmup, args.steps)
+        cur.wait_stream(cap)
+        torch.cuda.synchronize()
+        out.zero_()
+        lse.zero_()
+        g_warm.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(out, eager_out) and torch.equal(lse, eager_lse)):
+            raise RuntimeError("warmup graph replay differs from the eager decode")
+        out.zero_()
+        lse.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(cur)
+        g_timed.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ev_ms = [e0.elapsed_time(e1) / args.steps]
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    ev_ms = [a.elapsed_time(b) for a, b in evs]
     ev_mean = float(np.mean(ev_ms))
-    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step wall, "
-          f"{ev_mean * 1e3:.1f} us/call events (median {np.median(ev_ms) * 1e3:.1f})",
+    print(f"[bench] {args.steps} steps ({'eager' if args.eager else 'one graph'}): "
+          f"{ms_per_step * 1e3:.1f} us/step wall, {ev_mean * 1e3:.1f} us/step events",
           file=sys.stderr, flush=True)
+    if not (torch.equal(out, eager_out) and torch.equal(lse, eager_lse)):
+        raise RuntimeError("timed steps changed the decode result")
 
     tokens = float(sum(lens))
     value = tokens / (ms_per_step / 1e3)
@@ -135,13 +232,22 @@ def main():
              "frac": round(bw / PEAK_HBM_GBS, 4)} if hbm_bound else
             {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_MFMA_TFLOPS,
              "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_TFLOPS, 4)})
-    roof["traffic"] = None
-    roof["kernel"] = "mla_lowbit_decode call (decode_h16 + combine kernels)"
+    tr = measured_traffic(args.workload) if step is None else None
+    roof["traffic"] = tr["bytes_per_call"] if tr else None
+    roof["kernel"] = ("mla_lowbit_decode: decode_h16_kernel + combine_kernel"
+                      if step is None else
+                      "mla_lowbit_write_decode: write_kernel + decode_h16_kernel + combine_kernel")
     roof["algorithmic_bytes_per_launch"] = abytes
     roof["algorithmic_flops_per_launch"] = aflops
+    roof["hbm_frac"] = round(bw / PEAK_HBM_GBS, 4)
+    roof["mfma_frac"] = round(tf / PEAK_MFMA_TFLOPS, 4)
     roof["event_us_mean"] = round(ev_mean * 1e3, 2)
-    roof["event_us_p10_p50_p90"] = [round(float(np.percentile(ev_ms, q)) * 1e3, 2)
-                                   for q in (10, 50, 90)]
+    if args.eager:
+        roof["event_us_p10_p50_p90"] = [round(float(np.percentile(ev_ms, q)) * 1e3, 2)
+                                       for q in (10, 50, 90)]
+    if tr:
+        roof["traffic_fetch_write"] = [tr["fetch_bytes"], tr["write_bytes"]]
+        roof["traffic_copy_calibration"] = tr["copy_calibration"]
 
     cpu = None
     parity = None
@@ -159,11 +265,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4/int2 codes, fp16 MFMA, fp32 accumulate",
+        "dtype": "u4/u2 codes, f16 MFMA, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": wl.desc, "B": wl.B, "H": wl.H,
                    "format": "C4R4" if wl.c_bits == 4 else "C2R4",
-                   "tokens_per_step": int(tokens), "cache_copies_rotated": R},
+                   "tokens_per_step": int(tokens), "cache_copies_rotated": R,
+                   "launch": "eager" if args.eager else "one_hip_graph_of_K_steps"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity": parity,
@@ -172,8 +279,9 @@ def main():
 
 
 def cpu_baseline(cfg, wl, inp, step, out, lse, lens, budget_s):
-    """Time the CPU oracle's decode on a bounded sample of the same workload (whole
-    sequences, all heads), and check the GPU output on those rows."""
+    """Time the CPU oracle's decode on a bounded sample of the same workload:
+    whole sequences (all heads), shortest first, repeated in passes until about
+    budget_s seconds of oracle time; then check the GPU output on those rows."""
     import numpy as np
     import torch
 
@@ -187,54 +295,55 @@ def cpu_baseline(cfg, wl, inp, step, out, lse, lens, budget_s):
     final = np.array(lens, np.int32)
     D = 576
     seq_idx = inp.seq_idx
+    # one oracle cache for the sampled sequences (their page-table rows are disjoint)
+    op = np.zeros((inp.num_pages, oracle.page_bytes(oc)), np.uint8)
+    osink = np.zeros((wl.B, oc.n_sink, D), np.uint16)
+    olocal = np.zeros((wl.B, oc.n_local, D), np.uint16)
 
-    def oracle_state(seqs):
-        mask = torch.zeros(seq_idx.numel(), dtype=torch.bool, device=seq_idx.device)
-        for b in seqs:
-            mask |= seq_idx == b
-        op = np.zeros((inp.num_pages, oracle.page_bytes(oc)), np.uint8)
-        osink = np.zeros((wl.B, oc.n_sink, D), np.uint16)
-        olocal = np.zeros((wl.B, oc.n_local, D), np.uint16)
-        oracle.write(oc, u16(inp.c_kv[mask]), u16(inp.k_rope[mask]),
-                     seq_idx[mask].cpu().numpy(), inp.pos[mask].cpu().numpy(), pre, pt, op,
-                     osink, olocal)
+    def oracle_write(b):
+        mask = seq_idx == b
+        oracle.write(oc, u16(inp.c_kv[mask]), u16(inp.k_rope[mask]), seq_idx[mask].cpu().numpy(),
+                     inp.pos[mask].cpu().numpy(), pre, pt, op, osink, olocal)
         if step is not None:
-            sb = np.array(seqs, np.int32)
-            oracle.write(oc, u16(step.c_kv[seqs]), u16(step.k_rope[seqs]), sb,
+            sb = np.array([b], np.int32)
+            oracle.write(oc, u16(step.c_kv[[b]]), u16(step.k_rope[[b]]), sb,
                          step.pos.cpu().numpy()[sb], final, pt, op, osink, olocal)
-        return op, osink, olocal
 
     ql, qr = u16(inp.q_lat), u16(inp.q_rope)
-    order = list(np.argsort(final))  # shortest first, to fit the time budget
-    done, rows, refs, ref_lse = [], [], [], []
-    spent = 0.0
-    for b in order:
-        b = int(b)
-        op, osink, olocal = oracle_state([b])
-        sel = [(b, h) for h in range(wl.H)]
-        t0 = time.perf_counter()
-        ref, rl = oracle.decode(oc, synth.SOFTMAX_SCALE, ql, qr, op, pt, final, osink, olocal,
-                                sel=sel)
-        spent += time.perf_counter() - t0
-        done.append(b)
-        rows += sel
-        refs.append(ref)
-        ref_lse.append(rl)
-        if spent >= budget_s:
-            break
-        # estimated time of the next sequence
-        nxt = order[len(done)] if len(done) < len(order) else None
-        if nxt is None or spent + spent / sum(final[d] for d in done) * final[int(nxt)] > 2 * budget_s:
-            break
-    tok = float(sum(final[d] for d in done))
-    cpu = {"value": round(tok / spent, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+    order = [int(b) for b in np.argsort(final, kind="stable")]
+    done, refs, ref_lse = [], {}, {}
+    spent, n_tok, passes = 0.0, 0, 0
+    while spent < budget_s:
+        todo = order if passes == 0 else done
+        for b in todo:
+            if passes == 0:
+                # stop before a sequence that would overrun the budget by much
+                if done and spent + spent / n_tok * final[b] > 2 * budget_s:
+                    break
+                oracle_write(b)
+            sel = [(b, h) for h in range(wl.H)]
+            t0 = time.perf_counter()
+            ref, rl = oracle.decode(oc, synth.SOFTMAX_SCALE, ql, qr, op, pt, final, osink, olocal,
+                                    sel=sel)
+            spent += time.perf_counter() - t0
+            n_tok += int(final[b])
+            if passes == 0:
+                done.append(b)
+                refs[b], ref_lse[b] = ref, rl
+            if spent >= budget_s:
+                break
+        passes += 1
+    tok_seq = int(sum(final[d] for d in done))
+    cpu = {"value": round(n_tok / spent, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
            "kind": "oracle",
-           "sample": f"{len(done)} of {wl.B} sequences ({int(tok)} tokens) x all {wl.H} heads, "
-                     f"fp64 plain-loop decode, {spent:.1f} s"}
-    ref = np.concatenate(refs)
-    rl = np.concatenate(ref_lse)
+           "sample": f"{len(done)} of {wl.B} sequences ({tok_seq} cache tokens) x all {wl.H} "
+                     f"heads, fp64 plain-loop decode, {passes} pass(es), {n_tok} tokens attended "
+                     f"in {spent:.1f} s"}
+    rows = [(b, h) for b in done for h in range(wl.H)]
+    ref = np.concatenate([refs[b] for b in done])
+    rl = np.concatenate([ref_lse[b] for b in done])
     got = np.stack([out[b, h].float().cpu().numpy() for b, h in rows])
-    gl = np.array([lse[b, h].item() for b, h in rows])
+    gl = lse.cpu().numpy()[[b for b, _ in rows], [h for _, h in rows]]
     rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
     mx = float(np.max(np.abs(got - ref) / np.maximum(1.0, np.abs(ref))))
     dl = float(np.max(np.abs(gl - rl)))

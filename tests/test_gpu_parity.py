@@ -107,6 +107,73 @@ def test_decode_deterministic():
     assert torch.equal(l1, l2)
 
 
+def test_decode_graph_replay_matches_eager():
+    """A decode captured in a HIP graph and replayed several times, with eager
+    work on the same buffers between replays, gives the eager result each time."""
+    cfg = _cfg(4)
+    inp = synth.build_cache_inputs([5000, 130, 2100], 16, seed=13, device="cpu")
+    pages, sink, local = gpu_cache(cfg, inp, 3)
+    g = lambda t: t.to(DEV)  # noqa: E731
+    ql, qr, pt, sl = g(inp.q_lat), g(inp.q_rope), g(inp.page_table), g(inp.seq_lens)
+    ws = torch.empty(max(16, mla.decode_workspace_bytes(cfg, 3, 16, pt.shape[1])),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty(3, 16, 512, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(3, 16, dtype=torch.float32, device=DEV)
+
+    def run(stream=None):
+        mla.decode(cfg, ql, qr, pages, pt, sl, sink, local, synth.SOFTMAX_SCALE, out=out,
+                   lse=lse, workspace=ws, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        run(torch.cuda.current_stream())
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for k in range(4):
+        out.fill_(7.0)
+        lse.fill_(-1.0)
+        ws.fill_(0xFF)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), f"replay {k}"
+        assert torch.equal(lse, ref_l), f"replay {k}"
+        run()  # eager call between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16))
+
+
+def test_writer_drops_tokens_outside_the_table():
+    """Tokens of no sequence or beyond the page table are not written; the
+    valid ones are bit-exact."""
+    cfg = _cfg(4)
+    oc = ocfg_of(cfg)
+    inp = synth.build_cache_inputs([200, 64], 16, seed=17, device="cpu")
+    B, max_pages = 2, inp.page_table.shape[1]
+    op, osink, olocal = oracle_cache(oc, inp, B)
+    n = inp.seq_idx.numel()
+    bad_seq = torch.tensor([B, -1, 0, 1, 0], dtype=torch.int32)
+    bad_pos = torch.tensor([5, 5, max_pages * 64, -3, 1 << 30], dtype=torch.int32)
+    pick = torch.tensor([3, 7, 11, 100, 150])
+    c_kv = torch.cat([inp.c_kv, inp.c_kv[pick]])
+    k_rope = torch.cat([inp.k_rope, inp.k_rope[pick]])
+    seq_idx = torch.cat([inp.seq_idx, bad_seq])
+    pos = torch.cat([inp.pos, bad_pos])
+    pages, sink, local = mla.allocate_cache(cfg, B, inp.num_pages, DEV)
+    g = lambda t: t.to(DEV)  # noqa: E731
+    mla.write(cfg, g(c_kv), g(k_rope), g(seq_idx), g(pos), g(inp.seq_lens), g(inp.page_table),
+              pages, sink, local)
+    torch.cuda.synchronize()
+    assert n + 5 == seq_idx.numel()
+    assert np.array_equal(pages.cpu().numpy(), op)
+    assert np.array_equal(u16(sink), osink)
+    assert np.array_equal(u16(local), olocal)
+
+
 def test_serving_steps_across_the_window_edge():
     """Fused write+decode steps one token at a time as the sequences cross the
     sink/local boundaries; each step equals a from-scratch oracle build."""
