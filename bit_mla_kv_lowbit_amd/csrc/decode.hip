@@ -77,10 +77,11 @@ struct LaneOffsets {
 
 // Buffer descriptor of one physical page (raw byte addressing, range = page).
 template <int CB>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* pages, int pid) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* pages, int pid,
+                                                            bool any = true) {
   return __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(pages + (int64_t)pid * PageGeom<CB>::BYTES), (short)0, PageGeom<CB>::BYTES,
-      0x00020000);
+      (void*)(pages + (int64_t)pid * PageGeom<CB>::BYTES), (short)0,
+      any ? PageGeom<CB>::BYTES : 0, 0x00020000);
 }
 
 template <int CB>
@@ -419,11 +420,16 @@ __global__ __launch_bounds__(512, 1) void decode_h16_kernel(DecodeArgs a) {
   // set k mod 3 holds item it0 + k. Loads past the packed items repeat the last
   // packed page (in bounds, unused), which keeps the load/wait order static.
   const LaneOffsets<CB> lo(row, j, gs);
+  // Loads past the packed items repeat the last packed page; with no packed
+  // item the descriptor has an empty range (loads return 0, touch nothing).
+  // The loads stay unconditional so the wait counts are static and a wait for
+  // one page never waits for the prefetch issued after it.
   auto page_at = [&](int k) {
-    return page_rsrc<CB>(a.pages, __builtin_amdgcn_readfirstlane(pids[max(0, min(k, n_pk - 1))]));
+    const int pid = __builtin_amdgcn_readfirstlane(pids[max(0, min(k, n_pk - 1))]);
+    return page_rsrc<CB>(a.pages, n_pk > 0 ? pid : 0, n_pk > 0);
   };
   auto score_item = [&](PageRegs<CB>& cur, PageRegs<CB>& ahead, int k, _Float16* tbuf) {
-    if (n_pk > 0) load_page<CB>(ahead, page_at(k + 2), lo);
+    load_page<CB>(ahead, page_at(k + 2), lo);
     const int item = it0 + k;
     if (item < n_pp) {
       const int p0 = item * PAGE;
@@ -464,10 +470,8 @@ __global__ __launch_bounds__(512, 1) void decode_h16_kernel(DecodeArgs a) {
     return more;
   };
   if (n_it > 0) {
-    if (n_pk > 0) {
-      load_page<CB>(ra, page_at(0), lo);
-      load_page<CB>(rb, page_at(1), lo);
-    }
+    load_page<CB>(ra, page_at(0), lo);
+    load_page<CB>(rb, page_at(1), lo);
     put_scores(score_item(ra, rc, 0, tile));
     __syncthreads();
     if (w < 2) softmax_page(st, sxp, plds, alds, hh, tl, sl2);
