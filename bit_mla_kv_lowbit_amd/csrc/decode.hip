@@ -34,6 +34,8 @@
 #include "mla_common.h"
 #include "mla_kernels.h"
 
+#include <type_traits>
+
 namespace mla {
 
 constexpr float LN2 = 0.69314718055994530942f;
@@ -41,6 +43,9 @@ constexpr uint32_t MAGIC = 0x64006400u;  // fp16 pair (1024, 1024)
 constexpr uint32_t ONE_ZERO = 0x00003C00u;  // (s, z) = (1.0, 0.0): a BF16 token
 
 typedef __attribute__((address_space(3))) short4v lds_short4;
+
+constexpr int SXS = PAGE + 4;  // floats per partial-score row
+constexpr int PS = PAGE + 8;   // halves per P row
 
 __device__ __forceinline__ half2v as_h2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
 
@@ -170,14 +175,57 @@ __device__ __forceinline__ int group_channel(int lg, int gs, int j) {
   return lg < 8 ? GROUP * (8 * gs + lg) + 8 * j : D_C + GROUP * gs + 8 * j;
 }
 
+// Softmax and PV state of one wave.
+struct AttnState {
+  float4v oacc[4];     // O^T of channels 64w + 16mb + 4j + i, head t16
+  float m_run, l_run;  // running max (log2 domain) and sum of head hh (waves 0, 1)
+};
+
+// O^T[64 channels of wave w x 16 heads] += V^T P^T over one page's 64 tokens,
+// after rescaling by the page's factor; V^T is read transposed from the tile.
+// The eight MFMAs are issued one per code group from inside the next page's
+// score loop (pv_step), so their LDS reads and MFMA latency hide under the
+// score arithmetic.
+struct PvCtx {
+  const _Float16* tile;
+  half8 pB[2];
+};
+
+__device__ __forceinline__ void pv_begin(PvCtx& c, AttnState& st, const _Float16* tile,
+                                         const _Float16* plds, const float* alds, int j,
+                                         int t16) {
+  const float alpha = alds[t16];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) st.oacc[mb] *= alpha;
+  c.tile = tile;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+    c.pB[kb] = *reinterpret_cast<const half8*>(plds + t16 * PS + 32 * kb + 8 * j);
+}
+
+__device__ __forceinline__ void pv_step(AttnState& st, const PvCtx& c, int i, int w, int j,
+                                        int t16) {
+  const int mb = i >> 1, kb = i & 1;
+  const int trow = 32 * kb + 8 * j + (t16 >> 2);
+  const int col = 64 * w + 16 * mb + 4 * (t16 & 3);
+  const short4v lo =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(c.tile + tile_off(trow, col)));
+  const short4v hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(c.tile + tile_off(trow + 4, col)));
+  const half4 l4 = __builtin_bit_cast(half4, lo), h4 = __builtin_bit_cast(half4, hi);
+  const half8 av = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+  st.oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, c.pB[kb], st.oacc[mb], 0, 0, 0);
+}
+
 // Partial scores of one wave (S[i]: head 4j + i, its token) over its 9 groups,
 // plus the content tile rows of those groups. MASKED: a token with keep false
 // (protected, past the end or past the range) gets zero (scale, zero) words, so
 // its codes contribute 0, and a -inf score.
-template <int CB, bool MASKED>
+template <int CB, bool MASKED, bool PV>
 __device__ __forceinline__ float4v packed_scores(PageRegs<CB>& t, const half8 (&qA)[9],
                                                  const half8& qz, _Float16* tile, int row,
-                                                 int gs, int j, bool keep) {
+                                                 int gs, int j, bool keep, AttnState& st,
+                                                 const PvCtx& pv, int w, int t16) {
   if (MASKED) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -205,6 +253,7 @@ __device__ __forceinline__ float4v packed_scores(PageRegs<CB>& t, const half8 (&
   const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int lg = 0; lg < 9; ++lg) {
+    if (PV && lg < 8) pv_step(st, pv, lg, w, j, t16);
     const half8 c = group_codes<CB>(t, lg);
     const uint32_t sz = group_sz<CB>(t, lg);
     const float4v D = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[lg], c, zero4, 0, 0, 0);
@@ -219,9 +268,11 @@ __device__ __forceinline__ float4v packed_scores(PageRegs<CB>& t, const half8 (&
 // Partial scores and tile rows of a BF16 token (exact in fp16): one MFMA chain
 // over the wave's 9 groups; the 9 row pieces are loaded before use. Invalid
 // tokens read a valid row (in bounds) and are then zeroed / set to -inf.
+template <bool PV>
 __device__ __forceinline__ float4v bf16_scores(const uint16_t* rowp, bool valid,
                                                const half8 (&qA)[9], _Float16* tile, int row,
-                                               int gs, int j) {
+                                               int gs, int j, AttnState& st, const PvCtx& pv,
+                                               int w, int t16) {
   u32x4 raw[9];
 #pragma unroll
   for (int lg = 0; lg < 9; ++lg)
@@ -229,6 +280,7 @@ __device__ __forceinline__ float4v bf16_scores(const uint16_t* rowp, bool valid,
   float4v S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int lg = 0; lg < 9; ++lg) {
+    if (PV && lg < 8) pv_step(st, pv, lg, w, j, t16);
     half8 kv = bf16x8_to_f16x8(raw[lg]);
     kv = valid ? kv : (half8){};
     S = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[lg], kv, S, 0, 0, 0);
@@ -238,14 +290,7 @@ __device__ __forceinline__ float4v bf16_scores(const uint16_t* rowp, bool valid,
   return S;
 }
 
-constexpr int SXS = PAGE + 4;  // floats per partial-score row
-constexpr int PS = PAGE + 8;   // halves per P row
 
-// Softmax and PV state of one wave.
-struct AttnState {
-  float4v oacc[4];     // O^T of channels 64w + 16mb + 4j + i, head t16
-  float m_run, l_run;  // running max (log2 domain) and sum of head hh (waves 0, 1)
-};
 
 // Reductions over the 8 lanes of an aligned octet with DPP lane moves (no LDS
 // round trip): swap neighbours, swap pairs, then mirror within the half-row.
@@ -295,38 +340,6 @@ __device__ __forceinline__ void softmax_page(AttnState& st, const float* sxp, _F
   st.m_run = m_new;
   *reinterpret_cast<half8*>(plds + hh * PS + 8 * tl) = ph;
   if (tl == 0) alds[hh] = alpha;
-}
-
-// O^T[64 channels of wave w x 16 heads] += V^T P^T over one page's 64 tokens,
-// after rescaling by the page's factor; V^T is read transposed from the tile.
-__device__ __forceinline__ void pv_page(AttnState& st, const _Float16* tile, const _Float16* plds,
-                                        const float* alds, int w, int j, int t16) {
-  {
-    const float alpha = alds[t16];
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) st.oacc[mb] *= alpha;
-    }
-  }
-  half8 pB[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-    pB[kb] = *reinterpret_cast<const half8*>(plds + t16 * PS + 32 * kb + 8 * j);
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int trow = 32 * kb + 8 * j + (t16 >> 2);
-      const int col = 64 * w + 16 * mb + 4 * (t16 & 3);
-      const short4v lo =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(tile + tile_off(trow, col)));
-      const short4v hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(tile + tile_off(trow + 4, col)));
-      const half4 l4 = __builtin_bit_cast(half4, lo), h4 = __builtin_bit_cast(half4, hi);
-      const half8 av = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
-      st.oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pB[kb], st.oacc[mb], 0, 0, 0);
-    }
-  }
 }
 
 // Work items of a sequence: its packed pages (the pages that hold packed
@@ -416,27 +429,27 @@ __global__ __launch_bounds__(512, 1) void decode_h16_kernel(DecodeArgs a) {
   if (tid < n_pk) pids[tid] = a.page_table[(int64_t)b * a.max_pages + it0 + tid];
   __syncthreads();
 
-  // Packed items: two pages in flight ahead of the one being scored; register
-  // set k mod 3 holds item it0 + k. Loads past the packed items repeat the last
-  // packed page (in bounds, unused), which keeps the load/wait order static.
+  // Packed items: the page after the one being scored is in flight. Loads
+  // past the packed items repeat the last packed page; with no packed item the
+  // descriptor has an empty range (loads return 0, touch nothing). The loads
+  // stay unconditional so the wait counts are static and a wait for one page
+  // never waits for the prefetch issued after it.
   const LaneOffsets<CB> lo(row, j, gs);
-  // Loads past the packed items repeat the last packed page; with no packed
-  // item the descriptor has an empty range (loads return 0, touch nothing).
-  // The loads stay unconditional so the wait counts are static and a wait for
-  // one page never waits for the prefetch issued after it.
   auto page_at = [&](int k) {
     const int pid = __builtin_amdgcn_readfirstlane(pids[max(0, min(k, n_pk - 1))]);
     return page_rsrc<CB>(a.pages, n_pk > 0 ? pid : 0, n_pk > 0);
   };
-  auto score_item = [&](PageRegs<CB>& cur, PageRegs<CB>& ahead, int k, _Float16* tbuf) {
-    load_page<CB>(ahead, page_at(k + 2), lo);
+  auto score_item = [&](PageRegs<CB>& cur, int k, _Float16* tbuf, const PvCtx& pv,
+                        auto pv_tag) {
+    constexpr bool PV = decltype(pv_tag)::value;
     const int item = it0 + k;
     if (item < n_pp) {
       const int p0 = item * PAGE;
       if (p0 >= lo_p && p0 + PAGE <= hi_p)
-        return packed_scores<CB, false>(cur, qA, qz, tbuf, row, gs, j, true);
+        return packed_scores<CB, false, PV>(cur, qA, qz, tbuf, row, gs, j, true, st, pv, w, t16);
       const int p = p0 + row;
-      return packed_scores<CB, true>(cur, qA, qz, tbuf, row, gs, j, p >= lo_p && p < hi_p);
+      return packed_scores<CB, true, PV>(cur, qA, qz, tbuf, row, gs, j, p >= lo_p && p < hi_p, st,
+                                         pv, w, t16);
     }
     // BF16-protected tokens: q < n_s are the sink tokens, the rest the recent
     // window lo_start .. L - 1 (ring slots p mod n_local)
@@ -446,24 +459,33 @@ __global__ __launch_bounds__(512, 1) void decode_h16_kernel(DecodeArgs a) {
     const uint16_t* rowp =
         qc < n_s ? a.sink + ((int64_t)b * a.n_sink + qc) * D_ALL
                  : a.local + ((int64_t)b * a.n_local + (lo_start + qc - n_s) % a.n_local) * D_ALL;
-    return bf16_scores(rowp, valid, qA, tbuf, row, gs, j);
+    return bf16_scores<PV>(rowp, valid, qA, tbuf, row, gs, j, st, pv, w, t16);
   };
 
-  // Pipeline: the PV product of item k runs in the same phase as the scores of
-  // item k + 1 (double-buffered tile and P), so the MFMA / LDS work of one
-  // overlaps the VALU work of the other; two barriers per item. The loop is
-  // unrolled by three so each register set keeps its registers.
+  // Pipeline: the PV product of item k runs inside the score loop of item
+  // k + 1 (double-buffered tile and P), so the MFMA / LDS work of one overlaps
+  // the VALU work of the other; two barriers per item. Two register sets: the
+  // set that held item k is reloaded with item k + 2 at the start of the
+  // phase that scores item k + 1 (the loop is unrolled by two so each set
+  // keeps its registers).
   constexpr int TILE = PAGE * D_C, PL = 16 * PS;
-  PageRegs<CB> ra, rb, rc;
+  PageRegs<CB> ra, rb;
   auto put_scores = [&](const float4v& S) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sxp[(gs * 16 + 4 * j + i) * SXS + row] = S[i];
   };
   auto phase = [&](int k, PageRegs<CB>& cur, PageRegs<CB>& ahead) {
     const int cb = k & 1, nb = cb ^ 1;
-    pv_page(st, tile + cb * TILE, plds + cb * PL, alds, w, j, t16);
+    load_page<CB>(ahead, page_at(k + 2), lo);
+    PvCtx pv;
+    pv_begin(pv, st, tile + cb * TILE, plds + cb * PL, alds, j, t16);
     const bool more = k + 1 < n_it;
-    if (more) put_scores(score_item(cur, ahead, k + 1, tile + nb * TILE));
+    if (more) {
+      put_scores(score_item(cur, k + 1, tile + nb * TILE, pv, std::true_type()));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pv_step(st, pv, i, w, j, t16);
+    }
     __syncthreads();
     if (more && w < 2) softmax_page(st, sxp, plds + nb * PL, alds, hh, tl, sl2);
     __syncthreads();
@@ -472,14 +494,13 @@ __global__ __launch_bounds__(512, 1) void decode_h16_kernel(DecodeArgs a) {
   if (n_it > 0) {
     load_page<CB>(ra, page_at(0), lo);
     load_page<CB>(rb, page_at(1), lo);
-    put_scores(score_item(ra, rc, 0, tile));
+    put_scores(score_item(ra, 0, tile, PvCtx{}, std::false_type()));
     __syncthreads();
     if (w < 2) softmax_page(st, sxp, plds, alds, hh, tl, sl2);
     __syncthreads();
-    for (int k = 0;; k += 3) {
+    for (int k = 0;; k += 2) {
       if (!phase(k, rb, ra)) break;
-      if (!phase(k + 1, rc, rb)) break;
-      if (!phase(k + 2, ra, rc)) break;
+      if (!phase(k + 1, ra, rb)) break;
     }
   }
 
