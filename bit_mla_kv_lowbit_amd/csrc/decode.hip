@@ -355,7 +355,16 @@ __global__ __launch_bounds__(512, 1) void decode_h16_kernel(DecodeArgs a) {
   __shared__ float alds[16];
   __shared__ int pids[MAX_ITEMS];  // physical pages of this workgroup's packed items
 
-  const int split = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
+  // Workgroup -> (page range u = (b, split), head block hb). Consecutive
+  // workgroups go to the 8 XCDs in turn, and each XCD has its own L2: the head
+  // blocks of one page range get ids that are equal mod 8, so the page range is
+  // read from HBM once and served from that XCD's L2 to the other head blocks.
+  const int n_hb = a.H / 16;
+  const int gsz = 8 * n_hb;
+  const int u = (int)(blockIdx.x / gsz) * 8 + (int)(blockIdx.x % 8);
+  if (u >= a.B * a.n_split) return;  // padding of the last group of 8 ranges
+  const int hb = (int)(blockIdx.x % gsz) / 8;
+  const int b = u / a.n_split, split = u % a.n_split;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int lane = tid & 63, j = lane >> 4, t16 = lane & 15;
@@ -610,7 +619,8 @@ size_t decode_workspace_bytes(int B, int H, int max_pages) {
 
 hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
-  const dim3 grid(a.n_split, a.H / 16, a.B);
+  const int n_u = a.B * a.n_split;
+  const dim3 grid((n_u + 7) / 8 * 8 * (a.H / 16));
   if (c_bits == 4)
     decode_h16_kernel<4><<<grid, dim3(512), 0, stream>>>(a);
   else
