@@ -513,12 +513,28 @@ __global__ __launch_bounds__(512, 1) void decode_h16_kernel(DecodeArgs a) {
     }
   }
 
-  // partial result: O / l and its log-sum-exp (l and m live in the lanes that
-  // own each head's softmax)
+  // O / l and the log-sum-exp (l and m live in the lanes that own each head's
+  // softmax): the output itself when a sequence has a single page range, else
+  // the range's partial
   if (w < 2 && tl == 0) alds[hh] = st.l_run > 0.f ? 1.f / st.l_run : 0.f;
   __syncthreads();
-  const int64_t orow = ((int64_t)b * a.n_split + split) * H + h;
   const float inv = alds[t16];
+  if (a.n_split == 1) {
+    uint16_t* dst = a.out + ((int64_t)b * H + h) * D_C + 64 * w + 4 * j;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const float4v o = st.oacc[mb] * inv;
+      u32x2 packed;
+      packed.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
+      packed.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+      *reinterpret_cast<u32x2*>(dst + 16 * mb) = packed;
+    }
+    if (w < 2 && tl == 0)
+      a.lse[(int64_t)b * H + hb * 16 + hh] =
+          st.l_run > 0.f ? (st.m_run + __log2f(st.l_run)) * LN2 : -INFINITY;
+    return;
+  }
+  const int64_t orow = ((int64_t)b * a.n_split + split) * H + h;
   if (inv > 0.f) {
     float* dst = a.ws_o + orow * D_C + 64 * w + 4 * j;
 #pragma unroll
@@ -531,65 +547,59 @@ __global__ __launch_bounds__(512, 1) void decode_h16_kernel(DecodeArgs a) {
 }
 
 // Merge the page-range partials of one (sequence, head, 128-channel quarter):
-// lse = log sum exp(lse_s), out = sum_s exp(lse_s - lse) * o_s; empty ranges
-// (lse_s = -inf) carry weight 0 and are not read. The per-range weights are
-// computed once in LDS; then 8 split lanes x 32 channel lanes accumulate.
-
+// lse = log sum exp(lse_s), out = sum_s exp(lse_s - lse) * o_s. Eight split
+// lanes each fold their share of the ranges with a running max (empty ranges,
+// lse_s = -inf, are skipped), then the eight running states are merged.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-  __shared__ float wts[MAX_SPLITS];
-  __shared__ float red[8];
   __shared__ float4v part[8][32];
+  __shared__ float pm[8], pl[8];
   const int row = blockIdx.x >> 2, cq = blockIdx.x & 3;
   const int b = row / a.H, h = row % a.H;
   const int tid = threadIdx.x, sl = tid >> 5, ct = tid & 31;
   const int ns = a.n_split;
-  const float* lses = a.ws_lse + (int64_t)b * ns * a.H + h;
-
-  float m = -INFINITY;
-  for (int s = tid; s < ns; s += 256) {
-    const float v = lses[(int64_t)s * a.H];
-    wts[s] = v;
-    m = fmaxf(m, v);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((tid & 63) == 0) red[tid >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float sum = 0.f;
-  for (int s = tid; s < ns; s += 256) {
-    const float e = m == -INFINITY ? 0.f : __expf(wts[s] - m);
-    wts[s] = e;
-    sum += e;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-  if ((tid & 63) == 0) red[4 + (tid >> 6)] = sum;
-  __syncthreads();
-  sum = red[4] + red[5] + red[6] + red[7];
-  const float inv = sum > 0.f ? 1.f / sum : 0.f;
-
-  float4v acc = {0.f, 0.f, 0.f, 0.f};
   const int c0 = 128 * cq + 4 * ct;
+  const float* lses = a.ws_lse + (int64_t)b * ns * a.H + h;
   const float* base = a.ws_o + ((int64_t)b * ns * a.H + h) * D_C + c0;
   const int64_t stride = (int64_t)a.H * D_C;
+
+  float m = -INFINITY, l = 0.f;
+  float4v acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = sl; s < ns; s += 8) {
-    const float wgt = wts[s];
-    if (wgt != 0.f) acc += wgt * *reinterpret_cast<const float4v*>(base + s * stride);
+    const float ls = lses[(int64_t)s * a.H];
+    if (ls == -INFINITY) continue;
+    const float4v o = *reinterpret_cast<const float4v*>(base + s * stride);
+    const float m_new = fmaxf(m, ls);
+    const float fo = __expf(m - m_new), fs = __expf(ls - m_new);
+    acc = acc * fo + o * fs;
+    l = l * fo + fs;
+    m = m_new;
   }
   part[sl][ct] = acc;
+  if (ct == 0) {
+    pm[sl] = m;
+    pl[sl] = l;
+  }
   __syncthreads();
   if (sl == 0) {
+    float M = -INFINITY;
 #pragma unroll
-    for (int k = 1; k < 8; ++k) acc += part[k][ct];
-    acc *= inv;
+    for (int k = 0; k < 8; ++k) M = fmaxf(M, pm[k]);
+    float4v tot = {0.f, 0.f, 0.f, 0.f};
+    float lt = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (pm[k] == -INFINITY) continue;
+      const float f = __expf(pm[k] - M);
+      tot += part[k][ct] * f;
+      lt += pl[k] * f;
+    }
+    tot *= lt > 0.f ? 1.f / lt : 0.f;
     uint16_t* op = a.out + ((int64_t)b * a.H + h) * D_C + c0;
     u32x2 packed;
-    packed.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-    packed.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    packed.x = f32_to_bf16_rne(tot[0]) | (f32_to_bf16_rne(tot[1]) << 16);
+    packed.y = f32_to_bf16_rne(tot[2]) | (f32_to_bf16_rne(tot[3]) << 16);
     *reinterpret_cast<u32x2*>(op) = packed;
-    if (ct == 0 && cq == 0) a.lse[(int64_t)b * a.H + h] = sum > 0.f ? m + __logf(sum) : -INFINITY;
+    if (ct == 0 && cq == 0) a.lse[(int64_t)b * a.H + h] = lt > 0.f ? M + __logf(lt) : -INFINITY;
   }
 }
 
@@ -626,7 +636,7 @@ hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream) {
   else
     decode_h16_kernel<2><<<grid, dim3(512), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.n_split == 1) return e;  // one range: output written directly
   combine_kernel<<<dim3(a.B * a.H * 4), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }

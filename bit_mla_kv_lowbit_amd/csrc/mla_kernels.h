@@ -40,7 +40,7 @@ struct DecodeArgs {
 // Upper bound on partials per sequence that the combine kernel merges.
 constexpr int MAX_SPLITS = 2048;
 // Upper bound on work items (pages or protected-token chunks) per workgroup.
-constexpr int MAX_ITEMS = 128;
+constexpr int MAX_ITEMS = 256;
 
 struct SplitPlan {
   int n_split;
