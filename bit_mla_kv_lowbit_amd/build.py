@@ -13,6 +13,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed-fp32 instructions are generated for gfx950
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs (the decode scales each group's product on the VALU)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

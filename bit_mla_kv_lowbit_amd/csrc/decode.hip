@@ -6,31 +6,34 @@
 // aggregation (PV) product, and normalizes all valid tokens with one softmax.
 // The decode is the absorbed (MQA) form: all heads share the latent (GQLA card).
 //
-// Work decomposition: one workgroup of 8 wavefronts (two per SIMD) = one
+// Work decomposition: one workgroup of 4 wavefronts (one per SIMD) = one
 // (sequence, page range, 16-head block); the range is walked one 64-token page
 // per iteration, the next page's codes being loaded into registers while the
-// current one is used. Wave w takes the 16 tokens 16 (w & 3) .. +15 of the page
-// and half of the code groups (set w >> 2: content groups 8s .. 8s + 7 and RoPE
-// group s); lane (token t, sub-block j) holds the 8-channel sub-block j of each
-// of those groups (the code order makes one 128-bit load deliver one sub-block
-// of 4 (INT4) or 8 (INT2) groups). Per page:
-//   1. partial scores, exactly per group: the integer codes c (exact in fp16)
-//      are the B operand of v_mfma_f32_16x16x32_f16, one MFMA per 32-channel
-//      group gives D_g = q_g . c_g; then S = sum_g s_g D_g + sum_g z_g Q_g in
-//      fp32, with Q_g = sum of q over group g (the z term is one more MFMA with
-//      Q_g split into fp16 hi + lo). Rounding the reconstructed keys to fp16
-//      first would cost ~1e-3 in the scores of wide-range (outlier) groups;
+// current one is used. Wave w owns the 16 tokens 16w .. 16w + 15 of every page
+// for the scores and the softmax, and the 128 output channels 128w .. 128w + 127
+// for the PV product. Lane (token t, sub-block j) holds the 8-channel sub-block
+// j of each of its token's 18 code groups (16 content, 2 RoPE; the code order
+// makes one 128-bit load deliver one sub-block of 4 (INT4) or 8 (INT2) groups)
+// and all (scale, zero) words of its token. Per page:
+//   1. scores, exactly per group: the integer codes c (exact in fp16) are the
+//      B operand of v_mfma_f32_16x16x32_f16, one MFMA per 32-channel group
+//      gives D_g = q_g . c_g; then S = sum_g s_g D_g + sum_g z_g Q_g in fp32,
+//      with Q_g = sum of q over group g (the z term is two more MFMAs with Q_g
+//      split into fp16 hi + lo). Rounding the reconstructed keys to fp16 first
+//      would cost ~1e-3 in the scores of wide-range (outlier) groups;
 //   2. the reconstructed content values x = c * s + z (one packed fp16 FMA per
-//      channel pair) go to an LDS tile, token-major; the two partial scores of
-//      each token to a small LDS array;
-//   3. softmax once per head (wave w owns heads 2w, 2w + 1): running max and
-//      sum in the log2 domain, P in fp16 and each head's rescale factor to LDS;
-//   4. wave w accumulates O^T for channels 64w .. 64w + 63: the V^T operand is
-//      read from the token-major tile with ds_read_b64_tr_b16, P^T from LDS.
-// One extra workgroup per (sequence, head block) attends over the BF16-protected
-// tokens the same way (the page workgroups mask them out). The partials (O / l,
-// log-sum-exp) of all workgroups of a sequence are merged by combine_kernel
-// (split-K over the sequence with an LSE combine: one global softmax).
+//      channel pair) go to an LDS tile, token-major;
+//   3. softmax in the wave, with a reference max per head that all waves
+//      share: P = 2^(S log2e scale - M). M only moves when a score exceeds it
+//      by more than 2^8 (then the wave uses its own page max, publishes it, and
+//      every wave rescales by the same factors after the barrier), so P stays
+//      below 256 in fp16 and in the common case nothing is rescaled;
+//   4. after the page's one barrier, wave w accumulates O^T for its channels:
+//      V^T and P^T are read transposed from LDS with ds_read_b64_tr_b16.
+// The PV product of one page runs inside the score loop of the next one. The
+// partials (O / l, log-sum-exp) of the workgroups of a sequence are merged by
+// combine_kernel (split-K over the sequence with an LSE combine: one global
+// softmax); a sequence with a single page range writes its output directly.
 #include "mla_common.h"
 #include "mla_kernels.h"
 
@@ -40,14 +43,16 @@ namespace mla {
 
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr uint32_t MAGIC = 0x64006400u;  // fp16 pair (1024, 1024)
-constexpr uint32_t ONE_ZERO = 0x00003C00u;  // (s, z) = (1.0, 0.0): a BF16 token
+constexpr int WAVES = 4;                 // wavefronts per workgroup
+constexpr float TAU = 8.f;               // lazy-rescale threshold (log2 units)
+constexpr float M_NONE = -1e30f;         // reference max before any valid token
 
 typedef __attribute__((address_space(3))) short4v lds_short4;
-
-constexpr int SXS = PAGE + 4;  // floats per partial-score row
-constexpr int PS = PAGE + 8;   // halves per P row
+// read-only data read through the constant address space (scalar loads)
+typedef __attribute__((address_space(4))) const int32_t const_i32;
 
 __device__ __forceinline__ half2v as_h2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
+__device__ __forceinline__ uint32_t as_u32(half2v v) { return __builtin_bit_cast(uint32_t, v); }
 
 // (a & m) | o in one VALU op (the compiler otherwise emits an and plus an or)
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
@@ -55,32 +60,36 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
   return r;
 }
-__device__ __forceinline__ uint32_t as_u32(half2v v) { return __builtin_bit_cast(uint32_t, v); }
 
 // Raw data one lane loads for one page: sub-block j of its token in each of the
-// wave's 9 code groups, and those groups' (scale, zero) words.
+// 16 content groups and the 2 RoPE groups, and all (scale, zero) words of its
+// token.
 template <int CB>
 struct PageRegs {
-  u32x4 c[CB == 4 ? 2 : 1];  // content code chunks (8 groups)
-  u32x4 sz[2];               // content (s, z) words of the 8 groups
-  uint32_t r;                // RoPE code word (group 16 + set)
-  uint32_t rsz;              // RoPE (s, z) word
+  u32x4 c[CB == 4 ? 4 : 2];  // content code chunks
+  u32x4 sz[4];               // content (s, z) words of groups 0..15
+  u32x2 r;                   // RoPE code words (groups 0, 1)
+  u32x2 rsz;                 // RoPE (s, z) words
 };
 
-// Byte offsets, inside a page, of what one lane (slot, sub-block j, set gs) loads.
+// Byte offsets, inside a page, of what one lane (slot, sub-block j) loads,
+// relative to the start of each region (the region starts go in the scalar
+// offset of the buffer loads). The content code chunk m (16 bytes at + 64 m)
+// holds sub-block j of groups 4m .. 4m + 3 (INT4) or 8m .. 8m + 7 (INT2).
 template <int CB>
 struct LaneOffsets {
   uint32_t c, s, r, rs;
-  __device__ LaneOffsets(int slot, int j, int gs) {
+  __device__ LaneOffsets(int slot, int j) {
     using G = PageGeom<CB>;
-    c = G::OFF_CC + slot * G::CC + (CB == 4 ? 128 : 64) * gs + 16 * j;
-    s = G::OFF_CS + slot * G::CS + 32 * gs;
-    r = G::OFF_RC + slot * G::RC + 8 * j + 4 * gs;
-    rs = G::OFF_RS + slot * G::RS + 4 * gs;
+    c = slot * G::CC + 16 * j;
+    s = slot * G::CS;
+    r = slot * G::RC + 8 * j;
+    rs = slot * G::RS;
   }
 };
 
-// Buffer descriptor of one physical page (raw byte addressing, range = page).
+// Buffer descriptor of one physical page (raw byte addressing, range = page;
+// an empty range makes every load return 0 and touch nothing).
 template <int CB>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* pages, int pid,
                                                             bool any = true) {
@@ -92,14 +101,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* pages
 template <int CB>
 __device__ __forceinline__ void load_page(PageRegs<CB>& t, __amdgpu_buffer_rsrc_t rs,
                                           const LaneOffsets<CB>& o) {
+  using G = PageGeom<CB>;
 #pragma unroll
-  for (int m = 0; m < (CB == 4 ? 2 : 1); ++m)
-    t.c[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.c + 64 * m, 0, 0));
+  for (int m = 0; m < (CB == 4 ? 4 : 2); ++m)
+    t.c[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.c, G::OFF_CC + 64 * m, 0));
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
-    t.sz[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.s + 16 * m, 0, 0));
-  t.r = __builtin_amdgcn_raw_buffer_load_b32(rs, o.r, 0, 0);
-  t.rsz = __builtin_amdgcn_raw_buffer_load_b32(rs, o.rs, 0, 0);
+  for (int m = 0; m < 4; ++m)
+    t.sz[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.s, G::OFF_CS + 16 * m, 0));
+  t.r = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.r, G::OFF_RC, 0));
+  t.rsz = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.rs, G::OFF_RS, 0));
 }
 
 // Exact codes of channels 8j..8j+7 (pairs (0,1) (2,3) (4,5) (6,7)) of one group
@@ -131,17 +141,15 @@ __device__ __forceinline__ half8 codes2(uint32_t wd, int e) {
   return (half8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
-// Codes of local group lg (0..7: content group 8 set + lg; 8: RoPE group).
+// Codes and (s, z) word of content group g (0..15).
 template <int CB>
-__device__ __forceinline__ half8 group_codes(const PageRegs<CB>& t, int lg) {
-  if (lg == 8) return codes4(t.r);
-  if (CB == 4) return codes4(t.c[lg >> 2][lg & 3]);
-  return codes2(t.c[0][lg >> 1], lg & 1);
+__device__ __forceinline__ half8 content_codes(const PageRegs<CB>& t, int g) {
+  if (CB == 4) return codes4(t.c[g >> 2][g & 3]);
+  return codes2(t.c[g >> 3][(g & 7) >> 1], g & 1);
 }
-
 template <int CB>
-__device__ __forceinline__ uint32_t group_sz(const PageRegs<CB>& t, int lg) {
-  return lg == 8 ? t.rsz : t.sz[lg >> 2][lg & 3];
+__device__ __forceinline__ uint32_t content_sz(const PageRegs<CB>& t, int g) {
+  return t.sz[g >> 2][g & 3];
 }
 
 // Reconstructed fp16 values x = c * s + z (one rounding per value).
@@ -159,397 +167,494 @@ __device__ __forceinline__ half8 reconstruct(half8 c, uint32_t sz) {
   return r;
 }
 
-// LDS tile of reconstructed content values, 64 token rows x 512 fp16. The
-// 16-byte chunk index of each row is XOR-ed with f(row) so that (64 banks of
-// 4 bytes): a transposing read (8 rows 8j + x or 8j + 4 + x, x < 4, per 32
-// lanes, 32 bytes each) hits 8 distinct 32-byte bank segments (f bits 1..3 =
-// row bits 0, 1, 3; f bit 0 = row bit 2 is constant within one read), and a
-// row write (16 consecutive rows, one chunk each) hits 16 distinct chunks.
-__device__ __forceinline__ int tile_off(int row, int ch) {
-  const int f = ((row >> 2) & 1) | ((row & 3) << 1) | (((row >> 3) & 1) << 3);
-  return row * D_C + (((ch >> 3) ^ f) << 3) + (ch & 7);
+// z halves of two (s, z) words, packed
+__device__ __forceinline__ uint32_t z_pair(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
-// Channel (in the [content | rope] row) of sub-block j of local group lg of set gs.
-__device__ __forceinline__ int group_channel(int lg, int gs, int j) {
-  return lg < 8 ? GROUP * (8 * gs + lg) + 8 * j : D_C + GROUP * gs + 8 * j;
-}
+// LDS tile of reconstructed content values, 64 token rows x 512 fp16, rows
+// padded to TS halves (1040 bytes = 16 mod 256: 64 banks of 4 bytes). A row
+// write (16 lanes: 16 consecutive rows, 16 bytes each) hits 16 distinct 16-byte
+// bank slots. The PV operands map K slot jj (0..3) of lane group j to token
+// 8j + 2jj and slot 4 + jj to token 8j + 2jj + 1 (plus 32 per K-block), so a
+// transposing read (32 lanes: 8 rows 2 apart, 32 bytes each) hits 8 distinct
+// 32-byte bank segments. All per-lane addresses are a base plus constants.
+constexpr int TS = D_C + 8;
+// P buffer of one page, 64 token rows x 16 heads (fp16), rows padded to PS
+// halves (48 bytes): conflict-free row writes (8 bytes per lane) and the same
+// transposing reads as the tile.
+constexpr int PS = 24;
+constexpr int TILE = PAGE * TS;
 
-// Softmax and PV state of one wave.
+// Softmax and PV state of one lane: O^T of channels 128w + 16mb + 4j + i and
+// head t16; the reference max of head t16 (PV side) and of heads 4j + i
+// (score side: the same values, kept in both lane layouts) and the partial
+// sums of exp over the lane's tokens for heads 4j + i.
 struct AttnState {
-  float4v oacc[4];     // O^T of channels 64w + 16mb + 4j + i, head t16
-  float m_run, l_run;  // running max (log2 domain) and sum of head hh (waves 0, 1)
+  float4v oacc[8];
+  float m_pv;
+  float4v m_sc;
+  float4v l_sc;
+  float4v psum;  // this page's P of the lane's token, heads 4j + i (until folded into l_sc)
 };
 
-// O^T[64 channels of wave w x 16 heads] += V^T P^T over one page's 64 tokens,
-// after rescaling by the page's factor; V^T is read transposed from the tile.
-// The eight MFMAs are issued one per code group from inside the next page's
-// score loop (pv_step), so their LDS reads and MFMA latency hide under the
-// score arithmetic.
+// PV operands of one page: the tile it reads, P^T (B operand, K-blocks 0, 1)
+// and the V^T operand of the next PV step (read one step ahead).
 struct PvCtx {
   const _Float16* tile;
   half8 pB[2];
+  half8 av;
 };
 
-__device__ __forceinline__ void pv_begin(PvCtx& c, AttnState& st, const _Float16* tile,
-                                         const _Float16* plds, const float* alds, int j,
-                                         int t16) {
-  const float alpha = alds[t16];
+// Two transposing 8-byte reads (rows r and r + 1 of each lane's pattern) of one
+// 16-column block, as an 8-element operand.
+__device__ __forceinline__ half8 tr_pair(const _Float16* lo_p, const _Float16* hi_p) {
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)lo_p);
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)hi_p);
+  const half4 l4 = __builtin_bit_cast(half4, lo), h4 = __builtin_bit_cast(half4, hi);
+  return (half8){l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+}
+
+// V^T operand of PV step i = 2 mb + kb: channels of block mb of wave w, the 32
+// tokens of K-block kb.
+__device__ __forceinline__ half8 pv_load(const PvCtx& c, int i, int w, int j, int t16) {
+  const int mb = i >> 1, kb = i & 1;
+  const int trow = 32 * kb + 8 * j + 2 * (t16 >> 2);
+  const int col = 128 * w + 16 * mb + 4 * (t16 & 3);
+  return tr_pair(c.tile + trow * TS + col, c.tile + (trow + 1) * TS + col);
+}
+
+// O^T[16 channels, block mb of wave w x 16 heads] += V^T P^T over the 32 tokens
+// of K-block kb (step i = 2 mb + kb), after issuing the reads of step i + 1. The
+// sixteen steps are issued one per content group from inside the next page's
+// score loop.
+__device__ __forceinline__ void pv_step(AttnState& st, PvCtx& c, int i, int w, int j, int t16) {
+  const half8 cur = c.av;
+  if (i + 1 < 16) c.av = pv_load(c, i + 1, w, j, t16);
+  const int mb = i >> 1, kb = i & 1;
+  st.oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur, c.pB[kb], st.oacc[mb], 0, 0, 0);
+}
+
+// LDS exchange of one page between the score side and the PV side.
+struct PageLds {
+  _Float16* pbuf;  // [64 rows][PS]: 16 heads
+  float* mref;     // [4 waves][16 heads]: a wave's page reference max (when flagged)
+  int* flag;       // [4 waves]: the wave used its own page max
+};
+
+// Softmax of the wave's 16 tokens of a page, from the scores S (heads 4j + i,
+// the lane's token): P to the page's LDS buffer, the flag (and reference max)
+// of the wave, P of the lane's token kept in st.psum.
+__device__ __forceinline__ void softmax_tokens(AttnState& st, const float4v& S, const PageLds& pl,
+                                               float sl2, int w, int lane, int row, int j,
+                                               int t16) {
+  float4v t;
+  bool big = false;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) st.oacc[mb] *= alpha;
+  for (int i = 0; i < 4; ++i) {
+    t[i] = fmaf(S[i], sl2, -st.m_sc[i]);
+    big |= t[i] > TAU;
+  }
+  const bool any_big = __builtin_amdgcn_ballot_w64(big) != 0;
+  if (any_big) {
+    // the wave's own page max per head (over its 16 tokens: the 16 lanes of a
+    // row), at least the shared reference
+    float4v mx;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = S[i] * sl2;
+      v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true)));
+      v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true)));
+      v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true)));
+      v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true)));
+      mx[i] = fmaxf(st.m_sc[i], v);
+      t[i] = fmaf(S[i], sl2, -mx[i]);
+    }
+    if (t16 == 0) *reinterpret_cast<float4v*>(pl.mref + 16 * w + 4 * j) = mx;
+  }
+  if (lane == 0) pl.flag[w] = any_big ? 1 : 0;
+  float4v p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(t[i]);
+  st.psum = p;
+  u32x2 ph;
+  ph.x = as_u32((half2v){(_Float16)p[0], (_Float16)p[1]});
+  ph.y = as_u32((half2v){(_Float16)p[2], (_Float16)p[3]});
+  *reinterpret_cast<u32x2*>(pl.pbuf + row * PS + 4 * j) = ph;
+}
+
+// PV side of a page after its barrier: P^T operands, and the shared reference
+// max moved where a wave flagged it (O, the P operands and the partial sums
+// rescaled by the same factors in every wave, so all waves keep equal maxima).
+__device__ __forceinline__ void pv_begin(PvCtx& c, AttnState& st, const _Float16* tile,
+                                         const PageLds& pl, int w, int j, int t16) {
   c.tile = tile;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-    c.pB[kb] = *reinterpret_cast<const half8*>(plds + t16 * PS + 32 * kb + 8 * j);
+  for (int kb = 0; kb < 2; ++kb) {
+    const int trow = 32 * kb + 8 * j + 2 * (t16 >> 2);
+    c.pB[kb] = tr_pair(pl.pbuf + trow * PS + 4 * (t16 & 3), pl.pbuf + (trow + 1) * PS + 4 * (t16 & 3));
+  }
+  c.av = pv_load(c, 0, w, j, t16);
+  const int4 fl = *reinterpret_cast<const int4*>(pl.flag);
+  const int any = __builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w);
+  if (!any) {
+    st.l_sc += st.psum;
+    return;
+  }
+  const int f[4] = {fl.x, fl.y, fl.z, fl.w};
+  // PV side: head t16
+  float mp = st.m_pv;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v)
+    if (f[v]) mp = fmaxf(mp, pl.mref[16 * v + t16]);
+  const float alpha = __builtin_amdgcn_exp2f(st.m_pv - mp);
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) st.oacc[mb] *= alpha;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int src = 2 * kb + (j >> 1);  // wave that produced these 8 tokens
+    const float ref = f[src] ? pl.mref[16 * src + t16] : st.m_pv;
+    const float fs = __builtin_amdgcn_exp2f(ref - mp);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c.pB[kb][e] = (_Float16)((float)c.pB[kb][e] * fs);
+  }
+  st.m_pv = mp;
+  // score side: heads 4j + i, and this wave's partial sums of the page
+  float4v ms = st.m_sc;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) {
+    if (!f[v]) continue;
+    const float4v mr = *reinterpret_cast<const float4v*>(pl.mref + 16 * v + 4 * j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ms[i] = fmaxf(ms[i], mr[i]);
+  }
+  const float4v own = f[w] ? *reinterpret_cast<const float4v*>(pl.mref + 16 * w + 4 * j) : st.m_sc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    st.l_sc[i] = st.l_sc[i] * __builtin_amdgcn_exp2f(st.m_sc[i] - ms[i]) +
+                 st.psum[i] * __builtin_amdgcn_exp2f(own[i] - ms[i]);
+  st.m_sc = ms;
 }
 
-__device__ __forceinline__ void pv_step(AttnState& st, const PvCtx& c, int i, int w, int j,
-                                        int t16) {
-  const int mb = i >> 1, kb = i & 1;
-  const int trow = 32 * kb + 8 * j + (t16 >> 2);
-  const int col = 64 * w + 16 * mb + 4 * (t16 & 3);
-  const short4v lo =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(c.tile + tile_off(trow, col)));
-  const short4v hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(c.tile + tile_off(trow + 4, col)));
-  const half4 l4 = __builtin_bit_cast(half4, lo), h4 = __builtin_bit_cast(half4, hi);
-  const half8 av = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
-  st.oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, c.pB[kb], st.oacc[mb], 0, 0, 0);
-}
-
-// Partial scores of one wave (S[i]: head 4j + i, its token) over its 9 groups,
-// plus the content tile rows of those groups. MASKED: a token with keep false
-// (protected, past the end or past the range) gets zero (scale, zero) words, so
-// its codes contribute 0, and a -inf score.
-template <int CB, bool MASKED, bool PV>
-__device__ __forceinline__ float4v packed_scores(PageRegs<CB>& t, const half8 (&qA)[9],
-                                                 const half8& qz, _Float16* tile, int row,
-                                                 int gs, int j, bool keep, AttnState& st,
-                                                 const PvCtx& pv, int w, int t16) {
-  if (MASKED) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) t.sz[m][e] = keep ? t.sz[m][e] : 0u;
-    t.rsz = keep ? t.rsz : 0u;
-  }
-  // z term: lanes j = 0, 1 carry the z of the 8 content groups (matching the hi
-  // and lo parts of Q_g in qz), lanes j = 2, 3 the RoPE group's z in slot 0
-  half8 zb;
-  {
-    const half2v h0 = as_h2(__builtin_amdgcn_perm(t.sz[0].y, t.sz[0].x, 0x07060302u));
-    const half2v h1 = as_h2(__builtin_amdgcn_perm(t.sz[0].w, t.sz[0].z, 0x07060302u));
-    const half2v h2 = as_h2(__builtin_amdgcn_perm(t.sz[1].y, t.sz[1].x, 0x07060302u));
-    const half2v h3 = as_h2(__builtin_amdgcn_perm(t.sz[1].w, t.sz[1].z, 0x07060302u));
-    const _Float16 zr = as_h2(t.rsz).y;
-    const bool content = j < 2;
-    zb = (half8){content ? h0.x : zr, content ? h0.y : (_Float16)0.f,
-                 content ? h1.x : (_Float16)0.f, content ? h1.y : (_Float16)0.f,
-                 content ? h2.x : (_Float16)0.f, content ? h2.y : (_Float16)0.f,
-                 content ? h3.x : (_Float16)0.f, content ? h3.y : (_Float16)0.f};
-  }
-  float4v S = {0.f, 0.f, 0.f, 0.f};
-  S = __builtin_amdgcn_mfma_f32_16x16x32_f16(qz, zb, S, 0, 0, 0);
+// Scores of the lane's token (S[i]: head 4j + i) over its 18 groups, plus the
+// content tile row of the token.
+template <int CB>
+__device__ __forceinline__ float4v packed_scores(const PageRegs<CB>& t, const half8 (&qA)[18],
+                                                 const half8& qz1, const half8& qz2,
+                                                 _Float16* tile, int row, int j) {
+  // z operands (K slot 8j + i): zb1 holds the z of content groups 0..7 in lanes
+  // j < 2 and the RoPE groups' z in slots 0, 1 of lanes j >= 2; zb2 the z of
+  // content groups 8..15. qz1 / qz2 hold the matching fp16 hi (j even) and lo
+  // (j odd) parts of the group sums Q_g.
+  const bool lowj = j < 2;
+  const uint32_t rz = z_pair(t.rsz.x, t.rsz.y);
+  const u32x4 z1 = {lowj ? z_pair(t.sz[0].x, t.sz[0].y) : rz,
+                    lowj ? z_pair(t.sz[0].z, t.sz[0].w) : 0u,
+                    lowj ? z_pair(t.sz[1].x, t.sz[1].y) : 0u,
+                    lowj ? z_pair(t.sz[1].z, t.sz[1].w) : 0u};
+  const u32x4 z2 = {z_pair(t.sz[2].x, t.sz[2].y), z_pair(t.sz[2].z, t.sz[2].w),
+                    z_pair(t.sz[3].x, t.sz[3].y), z_pair(t.sz[3].z, t.sz[3].w)};
   const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
+  float4v S = __builtin_amdgcn_mfma_f32_16x16x32_f16(qz1, __builtin_bit_cast(half8, z1), zero4, 0, 0, 0);
+  S = __builtin_amdgcn_mfma_f32_16x16x32_f16(qz2, __builtin_bit_cast(half8, z2), S, 0, 0, 0);
+  // each group's product is scaled one group later, when its MFMA has finished
+  float4v Dp = zero4;
+  float sp = 0.f;
 #pragma unroll
-  for (int lg = 0; lg < 9; ++lg) {
-    if (PV && lg < 8) pv_step(st, pv, lg, w, j, t16);
-    const half8 c = group_codes<CB>(t, lg);
-    const uint32_t sz = group_sz<CB>(t, lg);
-    const float4v D = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[lg], c, zero4, 0, 0, 0);
-    S += (float)as_h2(sz).x * D;
-    if (lg < 8)
-      *reinterpret_cast<half8*>(tile + tile_off(row, group_channel(lg, gs, j))) = reconstruct(c, sz);
+  for (int g = 0; g < NG_C + NG_R; ++g) {
+    const half8 c = g < NG_C ? content_codes<CB>(t, g) : codes4(t.r[g - NG_C]);
+    const uint32_t sz = g < NG_C ? content_sz<CB>(t, g) : t.rsz[g - NG_C];
+    const float4v D = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[g], c, zero4, 0, 0, 0);
+    if (g > 0) S += sp * Dp;
+    if (g < NG_C)
+      *reinterpret_cast<half8*>(tile + row * TS + GROUP * g + 8 * j) = reconstruct(c, sz);
+    Dp = D;
+    sp = (float)as_h2(sz).x;
   }
-  if (MASKED && !keep) S = (float4v){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  S += sp * Dp;
   return S;
 }
 
-// Partial scores and tile rows of a BF16 token (exact in fp16): one MFMA chain
-// over the wave's 9 groups; the 9 row pieces are loaded before use. Invalid
-// tokens read a valid row (in bounds) and are then zeroed / set to -inf.
-template <bool PV>
-__device__ __forceinline__ float4v bf16_scores(const uint16_t* rowp, bool valid,
-                                               const half8 (&qA)[9], _Float16* tile, int row,
-                                               int gs, int j, AttnState& st, const PvCtx& pv,
-                                               int w, int t16) {
-  u32x4 raw[9];
+// Masked page: a token with keep false gets zero (scale, zero) words, so its
+// codes contribute 0 to the scores and the tile (its score is set to -inf).
+template <int CB>
+__device__ __forceinline__ void mask_token(PageRegs<CB>& t, bool keep) {
 #pragma unroll
-  for (int lg = 0; lg < 9; ++lg)
-    raw[lg] = *reinterpret_cast<const u32x4*>(rowp + group_channel(lg, gs, j));
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t.sz[m][e] = keep ? t.sz[m][e] : 0u;
+  t.rsz.x = keep ? t.rsz.x : 0u;
+  t.rsz.y = keep ? t.rsz.y : 0u;
+}
+
+// Channel of sub-block j of group g (0..15 content, 16, 17 RoPE) in a
+// [content | rope] row.
+__device__ __forceinline__ int group_channel(int g, int j) {
+  return g < NG_C ? GROUP * g + 8 * j : D_C + GROUP * (g - NG_C) + 8 * j;
+}
+
+// Scores and tile row of a token taken from the BF16 buffers (exact in fp16),
+// for the lanes with use set: one MFMA chain over the 18 groups. The other
+// lanes read a valid row (in bounds), contribute 0 and leave the tile alone.
+__device__ __forceinline__ float4v bf16_scores(const uint16_t* rowp, bool use,
+                                               const half8 (&qA)[18], _Float16* tile, int row,
+                                               int j) {
   float4v S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int lg = 0; lg < 9; ++lg) {
-    if (PV && lg < 8) pv_step(st, pv, lg, w, j, t16);
-    half8 kv = bf16x8_to_f16x8(raw[lg]);
-    kv = valid ? kv : (half8){};
-    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[lg], kv, S, 0, 0, 0);
-    if (lg < 8) *reinterpret_cast<half8*>(tile + tile_off(row, group_channel(lg, gs, j))) = kv;
+  for (int h = 0; h < 2; ++h) {
+    u32x4 raw[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i)
+      raw[i] = *reinterpret_cast<const u32x4*>(rowp + group_channel(9 * h + i, j));
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      const int g = 9 * h + i;
+      half8 kv = bf16x8_to_f16x8(raw[i]);
+      kv = use ? kv : (half8){};
+      S = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[g], kv, S, 0, 0, 0);
+      if (g < NG_C && use) *reinterpret_cast<half8*>(tile + row * TS + GROUP * g + 8 * j) = kv;
+    }
   }
-  if (!valid) S = (float4v){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   return S;
 }
 
-
-
-// Reductions over the 8 lanes of an aligned octet with DPP lane moves (no LDS
-// round trip): swap neighbours, swap pairs, then mirror within the half-row.
-__device__ __forceinline__ float octet_max(float v) {
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true)));
-  return v;
-}
-__device__ __forceinline__ float octet_sum(float v) {
+// Sum over the 16 lanes of a row (DPP butterfly: neighbours, pairs, half-row
+// mirror, row mirror).
+__device__ __forceinline__ float row_sum(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
   v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
   v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
   return v;
-}
-
-// Softmax of one page, once per head, by waves 0 and 1 (lane: head
-// hh = 8w + lane / 8, tokens 8 tl .. 8 tl + 7 with tl = lane % 8), from the two
-// partial scores in LDS; writes P (fp16) and each head's rescale factor.
-__device__ __forceinline__ void softmax_page(AttnState& st, const float* sxp, _Float16* plds,
-                                             float* alds, int hh, int tl, float sl2) {
-  float sv[8];
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-    const float4v a0 = *reinterpret_cast<const float4v*>(sxp + hh * SXS + 8 * tl + 4 * h2);
-    const float4v a1 = *reinterpret_cast<const float4v*>(sxp + (16 + hh) * SXS + 8 * tl + 4 * h2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sv[4 * h2 + i] = a0[i] + a1[i];
-  }
-  float mx = sv[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-  mx = octet_max(mx);
-  const float m_new = fmaxf(st.m_run, mx * sl2);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_use);
-  half8 ph;
-  float psum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float pv = __builtin_amdgcn_exp2f(fmaf(sv[i], sl2, -m_use));
-    psum += pv;
-    ph[i] = (_Float16)pv;
-  }
-  psum = octet_sum(psum);
-  st.l_run = st.l_run * alpha + psum;
-  st.m_run = m_new;
-  *reinterpret_cast<half8*>(plds + hh * PS + 8 * tl) = ph;
-  if (tl == 0) alds[hh] = alpha;
 }
 
 // Work items of a sequence: its packed pages (the pages that hold packed
 // tokens, protected tokens in them masked out), then its BF16-protected tokens
 // (sink, then recent window) in chunks of 64. Workgroup `split` takes items
-// [split * ipp, (split + 1) * ipp) with ipp = ceil(items / n_split), and writes
-// one partial (O / l, lse) that combine_kernel merges.
+// [split * n / n_split, (split + 1) * n / n_split) of the n items (an even
+// share), and writes one partial (O / l, lse) that combine_kernel merges.
 template <int CB>
-__global__ __launch_bounds__(512, 1) void decode_h16_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 tile[2 * PAGE * D_C];
-  __shared__ __attribute__((aligned(16))) float sxp[32 * SXS];
-  __shared__ __attribute__((aligned(16))) _Float16 plds[2 * 16 * PS];
-  __shared__ float alds[16];
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 tile[TILE];
+  __shared__ __attribute__((aligned(16))) _Float16 pbuf[PAGE * PS];
+  __shared__ __attribute__((aligned(16))) float mref[WAVES * 16];
+  __shared__ __attribute__((aligned(16))) int flag[WAVES];
+  __shared__ __attribute__((aligned(16))) float lsum[WAVES * 16];
   __shared__ int pids[MAX_ITEMS];  // physical pages of this workgroup's packed items
+
+  // All scalar arguments are read up front (one round trip, not one per first
+  // use: the length, the page table and the first page already form a chain
+  // of dependent reads, done with scalar loads so that they do not queue
+  // behind the vector reads of Q).
+  const int H = a.H, n_split = a.n_split, max_pages = a.max_pages;
+  const int n_sink = a.n_sink, n_local = a.n_local;
+  const uint16_t* const q_lat = a.q_lat;
+  const uint16_t* const q_rope = a.q_rope;
+  const int32_t* const seq_lens = a.seq_lens;
+  const int32_t* const page_table = a.page_table;
+  asm volatile("" ::"s"(H), "s"(n_split), "s"(max_pages), "s"(n_sink), "s"(n_local), "s"(q_lat),
+               "s"(q_rope), "s"(seq_lens), "s"(page_table), "s"(a.B));
 
   // Workgroup -> (page range u = (b, split), head block hb). Consecutive
   // workgroups go to the 8 XCDs in turn, and each XCD has its own L2: the head
   // blocks of one page range get ids that are equal mod 8, so the page range is
   // read from HBM once and served from that XCD's L2 to the other head blocks.
-  const int n_hb = a.H / 16;
+  const int n_hb = H / 16;
   const int gsz = 8 * n_hb;
   const int u = (int)(blockIdx.x / gsz) * 8 + (int)(blockIdx.x % 8);
-  if (u >= a.B * a.n_split) return;  // padding of the last group of 8 ranges
+  if (u >= a.B * n_split) return;  // padding of the last group of 8 ranges
   const int hb = (int)(blockIdx.x % gsz) / 8;
-  const int b = u / a.n_split, split = u % a.n_split;
+  const int b = __builtin_amdgcn_readfirstlane(u / n_split);
+  const int split = __builtin_amdgcn_readfirstlane(u % n_split);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int lane = tid & 63, j = lane >> 4, t16 = lane & 15;
-  const int gs = w >> 2;                  // code-group set of this wave
-  const int row = 16 * (w & 3) + t16;     // token row of this lane in the page / tile
-  const int hh = 8 * (w & 1) + (lane >> 3);  // softmax (waves 0, 1): head of this lane
-  const int tl = lane & 7;                   // softmax: tokens 8 tl .. 8 tl + 7
-  const int H = a.H;
+  const int row = 16 * w + t16;  // token row of this lane in the page / tile
   const int h = hb * 16 + t16;
+
+  // Q of the 16 heads is read once per workgroup (16 B per thread and chunk)
+  // and staged in the tile (rows of QS halves) before the waves take their
+  // operands from it.
+  constexpr int QS = D_ALL + 8;
+  constexpr int NCH = 16 * (D_ALL / 8);  // 8-channel chunks
+  u32x4 qv[(NCH + 255) / 256];
+  {
+    const uint16_t* ql = q_lat + ((int64_t)b * H + hb * 16) * D_C;
+    const uint16_t* qr = q_rope + ((int64_t)b * H + hb * 16) * D_R;
+#pragma unroll
+    for (int i = 0; i < (NCH + 255) / 256; ++i) {
+      const int c = min(tid + 256 * i, NCH - 1), hh = c / (D_ALL / 8), k = c % (D_ALL / 8);
+      qv[i] = *reinterpret_cast<const u32x4*>(k < D_C / 8 ? ql + hh * D_C + 8 * k
+                                                        : qr + hh * D_R + 8 * (k - D_C / 8));
+    }
+  }
+
   // lengths are clamped to what the page table can hold
-  const int L = min(max(a.seq_lens[b], 0), a.max_pages * PAGE);
+  const int L = min(max(*(const_i32*)(seq_lens + b), 0), max_pages * PAGE);
   const float sl2 = a.scale_log2;
 
-  // items of this sequence and of this workgroup
-  const int lo_p = a.n_sink, hi_p = L - a.n_local;       // packed: lo_p <= p < hi_p
-  const int n_pp = hi_p > lo_p ? (hi_p + PAGE - 1) / PAGE : 0;
-  const int n_s = min(a.n_sink, L);
-  const int lo_start = max(a.n_sink, L - a.n_local);
-  const int n_prot = n_s + max(0, L - lo_start);
-  const int n_items = n_pp + (n_prot + PAGE - 1) / PAGE;
-  const int ipp = (n_items + a.n_split - 1) / a.n_split;
-  const int it0 = min(split * ipp, n_items), it1 = min(it0 + ipp, n_items);
+  // Items of this sequence: its pages. Token p of a page is taken from the
+  // packed codes, or from the BF16 buffers if it is protected (p < n_sink:
+  // sink; p >= lo_start: the recent window, ring slot p mod n_local), or is
+  // masked if p >= L.
+  const int n_s = min(n_sink, L);
+  const int lo_start = max(n_sink, L - n_local);  // first token of the recent window
+  const int n_items = (L + PAGE - 1) / PAGE;
+  const int it0 = (int)((int64_t)split * n_items / n_split);
+  const int it1 = (int)((int64_t)(split + 1) * n_items / n_split);
   const int n_it = it1 - it0;
-  const int n_pk = max(0, min(it1, n_pp) - it0);  // packed items of this workgroup
+  const int n_pk = n_it;  // every item is a page of the page table
 
-  // Q as the A operand for the wave's 9 groups (lane = head t16; channels
-  // 8j .. 8j + 7 of each group), and qz: the z-term A operand holding the group
-  // sums Q_g split into fp16 hi (lanes j = 0, 2) and lo (j = 1, 3) parts, content
-  // groups in lanes j < 2, the RoPE group in slot 0 of lanes j >= 2.
-  half8 qA[9];
-  half8 qz;
+  // This workgroup's page ids, and the first page, which stays in flight
+  // while Q is converted. Loads past the last item repeat it; with no item
+  // the descriptor has an empty range (loads return 0, touch nothing), so
+  // the loads stay unconditional and the wait counts static.
+  const int* ptab = page_table + (int64_t)b * max_pages + it0;
+  const int pid_mine = tid < n_pk ? ptab[tid] : 0;
+  const LaneOffsets<CB> lo(row, j);
+  PageRegs<CB> regs;
+  const int pid0 = n_pk > 0 ? *(const_i32*)ptab : 0;
+  load_page<CB>(regs, page_rsrc<CB>(a.pages, pid0, n_pk > 0), lo);
+#pragma unroll
+  for (int i = 0; i < (NCH + 255) / 256; ++i) {
+    const int c = tid + 256 * i, hh = c / (D_ALL / 8), k = c % (D_ALL / 8);
+    if (c < NCH) *reinterpret_cast<u32x4*>(tile + hh * QS + 8 * k) = qv[i];
+  }
+  __syncthreads();  // Q staged
+
+  // Q as the A operand of the 18 groups (lane = head t16; channels 8j .. 8j + 7
+  // of each group), and the z-term A operands (see packed_scores).
+  half8 qA[NG_C + NG_R];
+  half8 qz1, qz2;
   {
-    const uint16_t* qrow_l = a.q_lat + ((int64_t)b * H + h) * D_C;
-    const uint16_t* qrow_r = a.q_rope + ((int64_t)b * H + h) * D_R;
-    u32x4 raw[9];
+    u32x4 qraw[NG_C + NG_R];
 #pragma unroll
-    for (int lg = 0; lg < 9; ++lg) {
-      const int ch = group_channel(lg, gs, j);
-      raw[lg] = *reinterpret_cast<const u32x4*>(ch < D_C ? qrow_l + ch : qrow_r + (ch - D_C));
-    }
-    float qs[9];
+    for (int g = 0; g < NG_C + NG_R; ++g)
+      qraw[g] = *reinterpret_cast<const u32x4*>(tile + t16 * QS + group_channel(g, j));
+    float qs[NG_C + NG_R];
 #pragma unroll
-    for (int lg = 0; lg < 9; ++lg) {
-      qA[lg] = bf16x8_to_f16x8(raw[lg]);
+    for (int g = 0; g < NG_C + NG_R; ++g) {
+      qA[g] = bf16x8_to_f16x8(qraw[g]);
       float sum = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        sum += bf16_to_f32(raw[lg][e] & 0xffffu) + bf16_to_f32(raw[lg][e] >> 16);
-      qs[lg] = sum;
+        sum += bf16_to_f32(qraw[g][e] & 0xffffu) + bf16_to_f32(qraw[g][e] >> 16);
+      qs[g] = sum;
     }
 #pragma unroll
-    for (int lg = 0; lg < 9; ++lg) {
-      qs[lg] += __shfl_xor(qs[lg], 16);
-      qs[lg] += __shfl_xor(qs[lg], 32);
+    for (int g = 0; g < NG_C + NG_R; ++g) {
+      qs[g] += __shfl_xor(qs[g], 16);
+      qs[g] += __shfl_xor(qs[g], 32);
     }
-    const bool lo_part = (j & 1) != 0, content = j < 2;
+    const bool lo_part = (j & 1) != 0, lowj = j < 2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float v = content ? qs[i] : (i == 0 ? qs[8] : 0.f);
-      const _Float16 hi = (_Float16)v;
-      qz[i] = lo_part ? (_Float16)(v - (float)hi) : hi;
+      const float v1 = lowj ? qs[i] : (i < NG_R ? qs[NG_C + i] : 0.f);
+      const float v2 = lowj ? qs[8 + i] : 0.f;
+      const _Float16 h1 = (_Float16)v1, h2 = (_Float16)v2;
+      qz1[i] = lo_part ? (_Float16)(v1 - (float)h1) : h1;
+      qz2[i] = lo_part ? (_Float16)(v2 - (float)h2) : h2;
     }
   }
 
   AttnState st;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) st.oacc[mb] = (float4v){0.f, 0.f, 0.f, 0.f};
-  st.m_run = -INFINITY;
-  st.l_run = 0.f;
+  for (int mb = 0; mb < 8; ++mb) st.oacc[mb] = (float4v){0.f, 0.f, 0.f, 0.f};
+  st.m_pv = M_NONE;
+  st.m_sc = (float4v){M_NONE, M_NONE, M_NONE, M_NONE};
+  st.l_sc = (float4v){0.f, 0.f, 0.f, 0.f};
+  st.psum = (float4v){0.f, 0.f, 0.f, 0.f};
 
-  if (tid < n_pk) pids[tid] = a.page_table[(int64_t)b * a.max_pages + it0 + tid];
-  __syncthreads();
+  if (tid < n_pk) pids[tid] = pid_mine;
+  __syncthreads();  // page ids in LDS; Q read out of the tile before it is overwritten
 
-  // Packed items: the page after the one being scored is in flight. Loads
-  // past the packed items repeat the last packed page; with no packed item the
-  // descriptor has an empty range (loads return 0, touch nothing). The loads
-  // stay unconditional so the wait counts are static and a wait for one page
-  // never waits for the prefetch issued after it.
-  const LaneOffsets<CB> lo(row, j, gs);
-  auto page_at = [&](int k) {
-    const int pid = __builtin_amdgcn_readfirstlane(pids[max(0, min(k, n_pk - 1))]);
-    return page_rsrc<CB>(a.pages, n_pk > 0 ? pid : 0, n_pk > 0);
-  };
-  auto score_item = [&](PageRegs<CB>& cur, int k, _Float16* tbuf, const PvCtx& pv,
-                        auto pv_tag) {
-    constexpr bool PV = decltype(pv_tag)::value;
-    const int item = it0 + k;
-    if (item < n_pp) {
-      const int p0 = item * PAGE;
-      if (p0 >= lo_p && p0 + PAGE <= hi_p)
-        return packed_scores<CB, false, PV>(cur, qA, qz, tbuf, row, gs, j, true, st, pv, w, t16);
-      const int p = p0 + row;
-      return packed_scores<CB, true, PV>(cur, qA, qz, tbuf, row, gs, j, p >= lo_p && p < hi_p, st,
-                                         pv, w, t16);
+  auto score_item = [&](const PageRegs<CB>& cur, int k) {
+    PageRegs<CB> t = cur;
+    const int p0 = (it0 + k) * PAGE;
+    const bool mixed = p0 < n_s || p0 + PAGE > lo_start;  // not every token packed
+    const int p = p0 + row;
+    const bool valid = p < L;
+    const bool prot = valid && (p < n_s || p >= lo_start);
+    if (mixed) mask_token<CB>(t, valid && !prot);
+    float4v S = packed_scores<CB>(t, qA, qz1, qz2, tile, row, j);
+    if (mixed) {
+      __builtin_amdgcn_sched_barrier(0);
+      const uint64_t pm = __builtin_amdgcn_ballot_w64(prot);
+      if (pm != 0) {
+        // lanes without a protected token read the first protected lane's row
+        const int src = (int)__builtin_ctzll(pm);
+        const int pp = prot ? p : __builtin_amdgcn_readlane(p, src);
+        const uint16_t* rowp = pp < n_s ? a.sink + ((int64_t)b * n_sink + pp) * D_ALL
+                                        : a.local + ((int64_t)b * n_local + pp % n_local) * D_ALL;
+        S += bf16_scores(rowp, prot, qA, tile, row, j);
+      }
+      if (!valid) S = (float4v){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
-    // BF16-protected tokens: q < n_s are the sink tokens, the rest the recent
-    // window lo_start .. L - 1 (ring slots p mod n_local)
-    const int q = (item - n_pp) * PAGE + row;
-    const bool valid = q < n_prot;
-    const int qc = min(q, n_prot - 1);
-    const uint16_t* rowp =
-        qc < n_s ? a.sink + ((int64_t)b * a.n_sink + qc) * D_ALL
-                 : a.local + ((int64_t)b * a.n_local + (lo_start + qc - n_s) % a.n_local) * D_ALL;
-    return bf16_scores<PV>(rowp, valid, qA, tbuf, row, gs, j, st, pv, w, t16);
+    return S;
   };
 
-  // Pipeline: the PV product of item k runs inside the score loop of item
-  // k + 1 (double-buffered tile and P), so the MFMA / LDS work of one overlaps
-  // the VALU work of the other; two barriers per item. Two register sets: the
-  // set that held item k is reloaded with item k + 2 at the start of the
-  // phase that scores item k + 1 (the loop is unrolled by two so each set
-  // keeps its registers).
-  constexpr int TILE = PAGE * D_C, PL = 16 * PS;
-  PageRegs<CB> ra, rb;
-  auto put_scores = [&](const float4v& S) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sxp[(gs * 16 + 4 * j + i) * SXS + row] = S[i];
-  };
-  auto phase = [&](int k, PageRegs<CB>& cur, PageRegs<CB>& ahead) {
-    const int cb = k & 1, nb = cb ^ 1;
-    load_page<CB>(ahead, page_at(k + 2), lo);
-    PvCtx pv;
-    pv_begin(pv, st, tile + cb * TILE, plds + cb * PL, alds, j, t16);
-    const bool more = k + 1 < n_it;
-    if (more) {
-      put_scores(score_item(cur, k + 1, tile + nb * TILE, pv, std::true_type()));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pv_step(st, pv, i, w, j, t16);
-    }
-    __syncthreads();
-    if (more && w < 2) softmax_page(st, sxp, plds + nb * PL, alds, hh, tl, sl2);
-    __syncthreads();
-    return more;
-  };
+  // Per item: scores, tile rows and softmax of the item, then (after a
+  // barrier) its PV product, then a barrier before the next item overwrites
+  // the tile. The next page's codes are loaded into the same registers as soon
+  // as the scores have used them, so they arrive during the PV product; two
+  // workgroups share each CU, so one's PV / barriers overlap the other's
+  // scores.
+  const PageLds pl{pbuf, mref, flag};
   if (n_it > 0) {
-    load_page<CB>(ra, page_at(0), lo);
-    load_page<CB>(rb, page_at(1), lo);
-    put_scores(score_item(ra, 0, tile, PvCtx{}, std::false_type()));
-    __syncthreads();
-    if (w < 2) softmax_page(st, sxp, plds, alds, hh, tl, sl2);
-    __syncthreads();
-    for (int k = 0;; k += 2) {
-      if (!phase(k, rb, ra)) break;
-      if (!phase(k + 1, ra, rb)) break;
+    for (int k = 0;; ++k) {
+      const int pid_next = pids[max(0, min(k + 1, n_pk - 1))];  // read ahead of its use
+      const float4v S = score_item(regs, k);
+      softmax_tokens(st, S, pl, sl2, w, lane, row, j, t16);
+      load_page<CB>(regs, page_rsrc<CB>(a.pages, n_pk > 0 ? __builtin_amdgcn_readfirstlane(pid_next) : 0,
+                                        n_pk > 0), lo);
+      __syncthreads();
+      PvCtx pv;
+      pv_begin(pv, st, tile, pl, w, j, t16);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pv_step(st, pv, i, w, j, t16);
+      if (k + 1 >= n_it) break;
+      __syncthreads();
     }
   }
 
-  // O / l and the log-sum-exp (l and m live in the lanes that own each head's
-  // softmax): the output itself when a sequence has a single page range, else
-  // the range's partial
-  if (w < 2 && tl == 0) alds[hh] = st.l_run > 0.f ? 1.f / st.l_run : 0.f;
-  __syncthreads();
-  const float inv = alds[t16];
-  if (a.n_split == 1) {
-    uint16_t* dst = a.out + ((int64_t)b * H + h) * D_C + 64 * w + 4 * j;
+  // l of each head: the lanes' partial sums (heads 4j + i) over the wave's 16
+  // tokens, then over the four waves; all waves hold the same reference max.
+  {
+    float4v l4 = st.l_sc;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int i = 0; i < 4; ++i) l4[i] = row_sum(l4[i]);
+    if (t16 == 0) *reinterpret_cast<float4v*>(lsum + 16 * w + 4 * j) = l4;
+  }
+  __syncthreads();
+  const float l = lsum[t16] + lsum[16 + t16] + lsum[32 + t16] + lsum[48 + t16];
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lse_v = l > 0.f ? (st.m_pv + __log2f(l)) * LN2 : -INFINITY;
+  if (n_split == 1) {
+    uint16_t* dst = a.out + ((int64_t)b * H + h) * D_C + 128 * w + 4 * j;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
       const float4v o = st.oacc[mb] * inv;
       u32x2 packed;
       packed.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
       packed.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
       *reinterpret_cast<u32x2*>(dst + 16 * mb) = packed;
     }
-    if (w < 2 && tl == 0)
-      a.lse[(int64_t)b * H + hb * 16 + hh] =
-          st.l_run > 0.f ? (st.m_run + __log2f(st.l_run)) * LN2 : -INFINITY;
+    if (w == 0 && j == 0) a.lse[(int64_t)b * H + h] = lse_v;
     return;
   }
-  const int64_t orow = ((int64_t)b * a.n_split + split) * H + h;
+  const int64_t orow = ((int64_t)b * n_split + split) * H + h;
   if (inv > 0.f) {
-    float* dst = a.ws_o + orow * D_C + 64 * w + 4 * j;
+    float* dst = a.ws_o + orow * D_C + 128 * w + 4 * j;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) *reinterpret_cast<float4v*>(dst + 16 * mb) = st.oacc[mb] * inv;
+    for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<float4v*>(dst + 16 * mb) = st.oacc[mb] * inv;
   }
-  if (w < 2 && tl == 0) {
-    const int64_t lrow = ((int64_t)b * a.n_split + split) * H + hb * 16 + hh;
-    a.ws_lse[lrow] = st.l_run > 0.f ? (st.m_run + __log2f(st.l_run)) * LN2 : -INFINITY;
-  }
+  if (w == 0 && j == 0) a.ws_lse[orow] = lse_v;
 }
 
 // Merge the page-range partials of one (sequence, head, 128-channel quarter):
 // lse = log sum exp(lse_s), out = sum_s exp(lse_s - lse) * o_s. Eight split
-// lanes each fold their share of the ranges with a running max (empty ranges,
-// lse_s = -inf, are skipped), then the eight running states are merged.
+// lanes each fold their share of the ranges relative to their own max, then
+// the eight states are merged.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   __shared__ float4v part[8][32];
   __shared__ float pm[8], pl[8];
@@ -562,17 +667,30 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const float* base = a.ws_o + ((int64_t)b * ns * a.H + h) * D_C + c0;
   const int64_t stride = (int64_t)a.H * D_C;
 
-  float m = -INFINITY, l = 0.f;
+  // this lane's max over its ranges, then their weighted sum: the loads of
+  // eight ranges are issued together (empty ranges, lse = -inf, hold no output)
+  float m = -INFINITY;
+  for (int s = sl; s < ns; s += 8) m = fmaxf(m, lses[(int64_t)s * a.H]);
+  float l = 0.f;
   float4v acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = sl; s < ns; s += 8) {
-    const float ls = lses[(int64_t)s * a.H];
-    if (ls == -INFINITY) continue;
-    const float4v o = *reinterpret_cast<const float4v*>(base + s * stride);
-    const float m_new = fmaxf(m, ls);
-    const float fo = __expf(m - m_new), fs = __expf(ls - m_new);
-    acc = acc * fo + o * fs;
-    l = l * fo + fs;
-    m = m_new;
+  if (m != -INFINITY) {
+    for (int s0 = sl; s0 < ns; s0 += 64) {
+      float ls[8];
+      float4v o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int s = min(s0 + 8 * u, ns - 1);
+        ls[u] = s0 + 8 * u < ns ? lses[(int64_t)s * a.H] : -INFINITY;
+        o[u] = *reinterpret_cast<const float4v*>(base + (int64_t)s * stride);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool ok = ls[u] != -INFINITY;
+        const float f = ok ? __expf(ls[u] - m) : 0.f;
+        l += f;
+        acc += ok ? o[u] * f : (float4v){0.f, 0.f, 0.f, 0.f};
+      }
+    }
   }
   part[sl][ct] = acc;
   if (ct == 0) {
@@ -604,14 +722,13 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 }
 
 SplitPlan plan_splits(int B, int H, int max_pages) {
-  // one 8-wave workgroup per CU (256 CUs) when the batch is small; enough
+  // two 4-wave workgroups per CU (256 CUs) when the batch is small; enough
   // workgroups that none takes more than MAX_ITEMS items (a sequence has at
-  // most max_pages packed pages plus 5 chunks of protected tokens, since
-  // n_sink + n_local <= 320)
+  // most max_pages pages)
   const int n_hb = H / 16;
   const int64_t base = (int64_t)(B > 0 ? B : 1) * n_hb;
-  int n = (int)(256 / base);
-  const int items = max_pages + 5;
+  int n = (int)(512 / base);
+  const int items = max_pages;
   const int need = (items + MAX_ITEMS - 1) / MAX_ITEMS;
   if (n < need) n = need;
   if (n > items) n = items;
@@ -632,9 +749,9 @@ hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream) {
   const int n_u = a.B * a.n_split;
   const dim3 grid((n_u + 7) / 8 * 8 * (a.H / 16));
   if (c_bits == 4)
-    decode_h16_kernel<4><<<grid, dim3(512), 0, stream>>>(a);
+    decode_kernel<4><<<grid, dim3(256), 0, stream>>>(a);
   else
-    decode_h16_kernel<2><<<grid, dim3(512), 0, stream>>>(a);
+    decode_kernel<2><<<grid, dim3(256), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;  // one range: output written directly
   combine_kernel<<<dim3(a.B * a.H * 4), dim3(256), 0, stream>>>(a);

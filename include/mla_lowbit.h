@@ -135,7 +135,9 @@ int mla_lowbit_write(const mla_lowbit_config* cfg, int n_tokens, const void* c_k
  *   lse[b,h] = log(sum_p exp(score[p]))                (fp32, natural log)
  * with c / k_rope read from BF16 buffers for protected tokens and
  * dequantized otherwise. A sequence of length 0 gives out = 0, lse = -inf;
- * seq_lens[b] is clamped to [0, max_pages * page_size].
+ * seq_lens[b] is clamped to [0, max_pages * page_size]. The pages of all
+ * tokens p < seq_lens[b] (page_table[b][0 .. ceil(L / 64))) must exist: every
+ * token has a packed copy, protected ones included.
  *   H            heads, a positive multiple of 16
  *   q_lat        bf16 [B, H, d_c];  q_rope  bf16 [B, H, d_r]
  *   out          bf16 [B, H, d_c];  lse     fp32 [B, H]
