@@ -77,8 +77,8 @@ DecodeArgs make_decode_args(const mla_lowbit_config* cfg, int B, int H, float so
   a.seq_lens = seq_lens;
   a.sink = static_cast<const uint16_t*>(sink);
   a.local = static_cast<const uint16_t*>(local);
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_lse = a.ws_o + (size_t)B * sp.n_split * H * D_C;
+  a.ws_lse = static_cast<float*>(workspace);
+  a.ws_o = reinterpret_cast<_Float16*>(a.ws_lse + (size_t)B * sp.n_split * H);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.B = B;

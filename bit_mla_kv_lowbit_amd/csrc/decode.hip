@@ -644,9 +644,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   }
   const int64_t orow = ((int64_t)b * n_split + split) * H + h;
   if (inv > 0.f) {
-    float* dst = a.ws_o + orow * D_C + 128 * w + 4 * j;
+    _Float16* dst = a.ws_o + orow * D_C + 128 * w + 4 * j;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<float4v*>(dst + 16 * mb) = st.oacc[mb] * inv;
+    for (int mb = 0; mb < 8; ++mb) {
+      const float4v o = st.oacc[mb] * inv;
+      u32x2 packed;
+      packed.x = as_u32((half2v){(_Float16)o[0], (_Float16)o[1]});
+      packed.y = as_u32((half2v){(_Float16)o[2], (_Float16)o[3]});
+      *reinterpret_cast<u32x2*>(dst + 16 * mb) = packed;
+    }
   }
   if (w == 0 && j == 0) a.ws_lse[orow] = lse_v;
 }
@@ -664,7 +670,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int ns = a.n_split;
   const int c0 = 128 * cq + 4 * ct;
   const float* lses = a.ws_lse + (int64_t)b * ns * a.H + h;
-  const float* base = a.ws_o + ((int64_t)b * ns * a.H + h) * D_C + c0;
+  const _Float16* base = a.ws_o + ((int64_t)b * ns * a.H + h) * D_C + c0;
   const int64_t stride = (int64_t)a.H * D_C;
 
   // this lane's max over its ranges, then their weighted sum: the loads of
@@ -681,7 +687,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
       for (int u = 0; u < 8; ++u) {
         const int s = min(s0 + 8 * u, ns - 1);
         ls[u] = s0 + 8 * u < ns ? lses[(int64_t)s * a.H] : -INFINITY;
-        o[u] = *reinterpret_cast<const float4v*>(base + (int64_t)s * stride);
+        const half4 o4 = *reinterpret_cast<const half4*>(base + (int64_t)s * stride);
+        o[u] = (float4v){(float)o4[0], (float)o4[1], (float)o4[2], (float)o4[3]};
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -741,7 +748,7 @@ SplitPlan plan_splits(int B, int H, int max_pages) {
 
 size_t decode_workspace_bytes(int B, int H, int max_pages) {
   const SplitPlan sp = plan_splits(B, H, max_pages);
-  return (size_t)B * sp.n_split * H * (D_C + 1) * sizeof(float);
+  return (size_t)B * sp.n_split * H * (sizeof(float) + D_C * sizeof(_Float16));
 }
 
 hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream) {

@@ -29,8 +29,8 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const uint16_t* sink;
   const uint16_t* local;
-  float* ws_o;    // [B, n_split, H, 512] fp32 partial outputs (normalized)
-  float* ws_lse;  // [B, n_split, H] fp32 partial log-sum-exp (natural log)
+  _Float16* ws_o;  // [B, n_split, H, 512] fp16 partial outputs (normalized)
+  float* ws_lse;   // [B, n_split, H] fp32 partial log-sum-exp (natural log)
   uint16_t* out;  // bf16 [B, H, 512]
   float* lse;     // fp32 [B, H]
   int B, H, n_split, pages_per_split, n_sink, n_local;
