@@ -428,11 +428,10 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
-// Work items of a sequence: its packed pages (the pages that hold packed
-// tokens, protected tokens in them masked out), then its BF16-protected tokens
-// (sink, then recent window) in chunks of 64. Workgroup `split` takes items
-// [split * n / n_split, (split + 1) * n / n_split) of the n items (an even
-// share), and writes one partial (O / l, lse) that combine_kernel merges.
+// Work items of a sequence: its pages (protected tokens taken from the BF16
+// buffers in their own slots). Workgroup `split` takes a contiguous range of
+// the pages (an even share of their cost), and writes one partial (O / l,
+// lse) that combine_kernel merges.
 template <int CB>
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 tile[TILE];
@@ -500,8 +499,25 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   const int n_s = min(n_sink, L);
   const int lo_start = max(n_sink, L - n_local);  // first token of the recent window
   const int n_items = (L + PAGE - 1) / PAGE;
-  const int it0 = (int)((int64_t)split * n_items / n_split);
-  const int it1 = (int)((int64_t)(split + 1) * n_items / n_split);
+  // Pages with protected tokens cost about twice a packed page (their BF16
+  // rows are read when they are scored), so the split boundaries balance
+  // the weight c(i) of pages 0 .. i - 1: one per page, plus one for the sink
+  // page and for each page from the one holding the window's first token.
+  const int wp = min(lo_start / PAGE, n_items);
+  const int sink_w = n_s > 0 ? 1 : 0;
+  auto weight_before = [&](int i) { return i + sink_w * min(i, 1) + max(0, i - wp); };
+  const int64_t W = weight_before(n_items);
+  auto first_item = [&](int s) {  // smallest i with c(i) >= s * W / n_split
+    int lo_i = 0, hi_i = n_items;
+    while (lo_i < hi_i) {
+      const int mid = (lo_i + hi_i) >> 1;
+      if ((int64_t)weight_before(mid) * n_split >= (int64_t)s * W) hi_i = mid;
+      else lo_i = mid + 1;
+    }
+    return lo_i;
+  };
+  const int it0 = first_item(split);
+  const int it1 = first_item(split + 1);  // it1 - it0 <= MAX_ITEMS by the split plan
   const int n_it = it1 - it0;
   const int n_pk = n_it;  // every item is a page of the page table
 
@@ -730,19 +746,19 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 
 SplitPlan plan_splits(int B, int H, int max_pages) {
   // two 4-wave workgroups per CU (256 CUs) when the batch is small; enough
-  // workgroups that none takes more than MAX_ITEMS items (a sequence has at
-  // most max_pages pages)
+  // workgroups that none takes more than MAX_ITEMS pages: a share of the page
+  // weight (at most max_pages + 6: the sink page and at most 5 pages of a
+  // 256-token window weigh 2) spans at most its weight + 3 pages
   const int n_hb = H / 16;
   const int64_t base = (int64_t)(B > 0 ? B : 1) * n_hb;
   int n = (int)(512 / base);
-  const int items = max_pages;
-  const int need = (items + MAX_ITEMS - 1) / MAX_ITEMS;
+  const int need = (max_pages + 6 + (MAX_ITEMS - 3) - 1) / (MAX_ITEMS - 3);
   if (n < need) n = need;
-  if (n > items) n = items;
+  if (n > max_pages) n = max_pages;
   if (n < 1) n = 1;
   SplitPlan sp;
   sp.n_split = n;
-  sp.pages_per_split = (items + n - 1) / n;  // upper bound, informational
+  sp.pages_per_split = (max_pages + n - 1) / n;  // informational
   return sp;
 }
 
