@@ -547,20 +547,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < NG_C + NG_R; ++g)
       qraw[g] = *reinterpret_cast<const u32x4*>(tile + t16 * QS + group_channel(g, j));
+    // group sums Q_g of head t16: one MFMA with a ones A operand (Q as the B
+    // operand has the same lane layout as the A operand)
     float qs[NG_C + NG_R];
+    const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+    const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g = 0; g < NG_C + NG_R; ++g) {
       qA[g] = bf16x8_to_f16x8(qraw[g]);
-      float sum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        sum += bf16_to_f32(qraw[g][e] & 0xffffu) + bf16_to_f32(qraw[g][e] >> 16);
-      qs[g] = sum;
-    }
-#pragma unroll
-    for (int g = 0; g < NG_C + NG_R; ++g) {
-      qs[g] += __shfl_xor(qs[g], 16);
-      qs[g] += __shfl_xor(qs[g], 32);
+      qs[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, qA[g], zero4, 0, 0, 0)[0];
     }
     const bool lo_part = (j & 1) != 0, lowj = j < 2;
 #pragma unroll
