@@ -234,9 +234,9 @@ def main():
              "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_TFLOPS, 4)})
     tr = measured_traffic(args.workload) if step is None else None
     roof["traffic"] = tr["bytes_per_call"] if tr else None
-    roof["kernel"] = ("mla_lowbit_decode: decode_h16_kernel + combine_kernel"
+    roof["kernel"] = ("mla_lowbit_decode: decode_kernel + combine_kernel"
                       if step is None else
-                      "mla_lowbit_write_decode: write_kernel + decode_h16_kernel + combine_kernel")
+                      "mla_lowbit_write_decode: write_kernel + decode_kernel + combine_kernel")
     roof["algorithmic_bytes_per_launch"] = abytes
     roof["algorithmic_flops_per_launch"] = aflops
     roof["hbm_frac"] = round(bw / PEAK_HBM_GBS, 4)

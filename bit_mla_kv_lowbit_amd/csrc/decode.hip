@@ -668,75 +668,80 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   if (w == 0 && j == 0) a.ws_lse[orow] = lse_v;
 }
 
-// Merge the page-range partials of one (sequence, head, 128-channel quarter):
-// lse = log sum exp(lse_s), out = sum_s exp(lse_s - lse) * o_s. Eight split
-// lanes each fold their share of the ranges relative to their own max, then
-// the eight states are merged.
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-  __shared__ float4v part[8][32];
-  __shared__ float pm[8], pl[8];
-  const int row = blockIdx.x >> 2, cq = blockIdx.x & 3;
+// Merge the page-range partials of one (sequence, head): lse = log sum
+// exp(lse_s), out = sum_s exp(lse_s - lse) * o_s. SL split lanes (SL = 1, 2,
+// 4 or 8, at least min(n_split, 8)) x 64 channel lanes of 8 channels: each
+// split lane folds its share of the ranges relative to its own max, issuing
+// the loads of four ranges together (empty ranges, lse = -inf, hold no
+// output), then the SL states are merged in LDS.
+template <int SL>
+__global__ __launch_bounds__(SL * 64) void combine_kernel(DecodeArgs a) {
+  __shared__ float part[SL][8][64];
+  __shared__ float pm[SL], pl[SL];
+  const int row = blockIdx.x;
   const int b = row / a.H, h = row % a.H;
-  const int tid = threadIdx.x, sl = tid >> 5, ct = tid & 31;
+  const int tid = threadIdx.x, sl = tid >> 6, cl = tid & 63;
   const int ns = a.n_split;
-  const int c0 = 128 * cq + 4 * ct;
   const float* lses = a.ws_lse + (int64_t)b * ns * a.H + h;
-  const _Float16* base = a.ws_o + ((int64_t)b * ns * a.H + h) * D_C + c0;
+  const _Float16* base = a.ws_o + ((int64_t)b * ns * a.H + h) * D_C + 8 * cl;
   const int64_t stride = (int64_t)a.H * D_C;
 
-  // this lane's max over its ranges, then their weighted sum: the loads of
-  // eight ranges are issued together (empty ranges, lse = -inf, hold no output)
   float m = -INFINITY;
-  for (int s = sl; s < ns; s += 8) m = fmaxf(m, lses[(int64_t)s * a.H]);
+  for (int s = sl; s < ns; s += SL) m = fmaxf(m, lses[(int64_t)s * a.H]);
   float l = 0.f;
-  float4v acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (m != -INFINITY) {
-    for (int s0 = sl; s0 < ns; s0 += 64) {
-      float ls[8];
-      float4v o[8];
+    for (int s0 = sl; s0 < ns; s0 += 4 * SL) {
+      float ls[4];
+      half8 o[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int s = min(s0 + 8 * u, ns - 1);
-        ls[u] = s0 + 8 * u < ns ? lses[(int64_t)s * a.H] : -INFINITY;
-        const half4 o4 = *reinterpret_cast<const half4*>(base + (int64_t)s * stride);
-        o[u] = (float4v){(float)o4[0], (float)o4[1], (float)o4[2], (float)o4[3]};
+      for (int u = 0; u < 4; ++u) {
+        const int s = min(s0 + SL * u, ns - 1);
+        ls[u] = s0 + SL * u < ns ? lses[(int64_t)s * a.H] : -INFINITY;
+        o[u] = *reinterpret_cast<const half8*>(base + (int64_t)s * stride);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 4; ++u) {
         const bool ok = ls[u] != -INFINITY;
         const float f = ok ? __expf(ls[u] - m) : 0.f;
         l += f;
-        acc += ok ? o[u] * f : (float4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += ok ? (float)o[u][e] * f : 0.f;
       }
     }
   }
-  part[sl][ct] = acc;
-  if (ct == 0) {
-    pm[sl] = m;
-    pl[sl] = l;
-  }
-  __syncthreads();
-  if (sl == 0) {
+  if (SL > 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[sl][e][cl] = acc[e];
+    if (cl == 0) {
+      pm[sl] = m;
+      pl[sl] = l;
+    }
+    __syncthreads();
+    if (sl != 0) return;
     float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) M = fmaxf(M, pm[k]);
-    float4v tot = {0.f, 0.f, 0.f, 0.f};
-    float lt = 0.f;
+    for (int k = 0; k < SL; ++k) M = fmaxf(M, pm[k]);
+    l = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < SL; ++k) {
       if (pm[k] == -INFINITY) continue;
       const float f = __expf(pm[k] - M);
-      tot += part[k][ct] * f;
-      lt += pl[k] * f;
+      l += pl[k] * f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += part[k][e][cl] * f;
     }
-    tot *= lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* op = a.out + ((int64_t)b * a.H + h) * D_C + c0;
-    u32x2 packed;
-    packed.x = f32_to_bf16_rne(tot[0]) | (f32_to_bf16_rne(tot[1]) << 16);
-    packed.y = f32_to_bf16_rne(tot[2]) | (f32_to_bf16_rne(tot[3]) << 16);
-    *reinterpret_cast<u32x2*>(op) = packed;
-    if (ct == 0 && cq == 0) a.lse[(int64_t)b * a.H + h] = lt > 0.f ? M + __logf(lt) : -INFINITY;
+    m = M;
   }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  u32x4 packed;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    packed[e] = f32_to_bf16_rne(acc[2 * e] * inv) | (f32_to_bf16_rne(acc[2 * e + 1] * inv) << 16);
+  *reinterpret_cast<u32x4*>(a.out + ((int64_t)b * a.H + h) * D_C + 8 * cl) = packed;
+  if (cl == 0) a.lse[(int64_t)b * a.H + h] = l > 0.f ? m + __logf(l) : -INFINITY;
 }
 
 SplitPlan plan_splits(int B, int H, int max_pages) {
@@ -772,7 +777,13 @@ hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream) {
     decode_kernel<2><<<grid, dim3(256), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;  // one range: output written directly
-  combine_kernel<<<dim3(a.B * a.H * 4), dim3(256), 0, stream>>>(a);
+  const dim3 cgrid(a.B * a.H);
+  if (a.n_split >= 8)
+    combine_kernel<8><<<cgrid, dim3(512), 0, stream>>>(a);
+  else if (a.n_split >= 4)
+    combine_kernel<4><<<cgrid, dim3(256), 0, stream>>>(a);
+  else
+    combine_kernel<2><<<cgrid, dim3(128), 0, stream>>>(a);
   return hipGetLastError();
 }
 
