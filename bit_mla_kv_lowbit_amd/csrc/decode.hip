@@ -669,79 +669,84 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 }
 
 // Merge the page-range partials of one (sequence, head): lse = log sum
-// exp(lse_s), out = sum_s exp(lse_s - lse) * o_s. SL split lanes (SL = 1, 2,
-// 4 or 8, at least min(n_split, 8)) x 64 channel lanes of 8 channels: each
-// split lane folds its share of the ranges relative to its own max, issuing
-// the loads of four ranges together (empty ranges, lse = -inf, hold no
-// output), then the SL states are merged in LDS.
-template <int SL>
-__global__ __launch_bounds__(SL * 64) void combine_kernel(DecodeArgs a) {
-  __shared__ float part[SL][8][64];
+// exp(lse_s), out = sum_s exp(lse_s - lse) * o_s. A workgroup takes SL split
+// lanes x CL channel lanes of 8 channels (64 / CL workgroups per row). Each
+// split lane issues the loads of up to eight of its ranges together and folds
+// them with a running max (empty ranges, lse = -inf, hold no output); the SL
+// states are then merged in LDS.
+template <int SL, int CL>
+__global__ __launch_bounds__(SL * CL) void combine_kernel(DecodeArgs a) {
+  __shared__ float part[SL][8][CL];
   __shared__ float pm[SL], pl[SL];
-  const int row = blockIdx.x;
+  constexpr int PER_ROW = 64 / CL;
+  const int row = blockIdx.x / PER_ROW, cq = blockIdx.x % PER_ROW;
   const int b = row / a.H, h = row % a.H;
-  const int tid = threadIdx.x, sl = tid >> 6, cl = tid & 63;
+  const int tid = threadIdx.x, sl = tid / CL, cl = tid % CL;
+  const int ch = 8 * (cq * CL + cl);
   const int ns = a.n_split;
   const float* lses = a.ws_lse + (int64_t)b * ns * a.H + h;
-  const _Float16* base = a.ws_o + ((int64_t)b * ns * a.H + h) * D_C + 8 * cl;
+  const _Float16* base = a.ws_o + ((int64_t)b * ns * a.H + h) * D_C + ch;
   const int64_t stride = (int64_t)a.H * D_C;
 
-  float m = -INFINITY;
-  for (int s = sl; s < ns; s += SL) m = fmaxf(m, lses[(int64_t)s * a.H]);
-  float l = 0.f;
+  float m = -INFINITY, l = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (m != -INFINITY) {
-    for (int s0 = sl; s0 < ns; s0 += 4 * SL) {
-      float ls[4];
-      half8 o[4];
+  for (int s0 = sl; s0 < ns; s0 += 8 * SL) {
+    float ls[8];
+    half8 o[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int s = min(s0 + SL * u, ns - 1);
-        ls[u] = s0 + SL * u < ns ? lses[(int64_t)s * a.H] : -INFINITY;
-        o[u] = *reinterpret_cast<const half8*>(base + (int64_t)s * stride);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bool ok = ls[u] != -INFINITY;
-        const float f = ok ? __expf(ls[u] - m) : 0.f;
-        l += f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += ok ? (float)o[u][e] * f : 0.f;
-      }
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + SL * u, ns - 1);
+      ls[u] = s0 + SL * u < ns ? lses[(int64_t)s * a.H] : -INFINITY;
+      o[u] = *reinterpret_cast<const half8*>(base + (int64_t)s * stride);
     }
+    float mc = ls[0];
+#pragma unroll
+    for (int u = 1; u < 8; ++u) mc = fmaxf(mc, ls[u]);
+    if (mc == -INFINITY) continue;
+    const float m_new = fmaxf(m, mc);
+    const float r = __expf(m - m_new);  // 0 while m = -inf
+    l *= r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= r;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = ls[u] != -INFINITY;
+      const float f = ok ? __expf(ls[u] - m_new) : 0.f;
+      l += f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += ok ? (float)o[u][e] * f : 0.f;
+    }
+    m = m_new;
   }
-  if (SL > 1) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) part[sl][e][cl] = acc[e];
-    if (cl == 0) {
-      pm[sl] = m;
-      pl[sl] = l;
-    }
-    __syncthreads();
-    if (sl != 0) return;
-    float M = -INFINITY;
+  for (int e = 0; e < 8; ++e) part[sl][e][cl] = acc[e];
+  if (cl == 0) {
+    pm[sl] = m;
+    pl[sl] = l;
+  }
+  __syncthreads();
+  if (sl != 0) return;
+  float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < SL; ++k) M = fmaxf(M, pm[k]);
-    l = 0.f;
+  for (int k = 0; k < SL; ++k) M = fmaxf(M, pm[k]);
+  l = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int k = 0; k < SL; ++k) {
-      if (pm[k] == -INFINITY) continue;
-      const float f = __expf(pm[k] - M);
-      l += pl[k] * f;
+  for (int k = 0; k < SL; ++k) {
+    if (pm[k] == -INFINITY) continue;
+    const float f = __expf(pm[k] - M);
+    l += pl[k] * f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += part[k][e][cl] * f;
-    }
-    m = M;
+    for (int e = 0; e < 8; ++e) acc[e] += part[k][e][cl] * f;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   u32x4 packed;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     packed[e] = f32_to_bf16_rne(acc[2 * e] * inv) | (f32_to_bf16_rne(acc[2 * e + 1] * inv) << 16);
-  *reinterpret_cast<u32x4*>(a.out + ((int64_t)b * a.H + h) * D_C + 8 * cl) = packed;
-  if (cl == 0) a.lse[(int64_t)b * a.H + h] = l > 0.f ? m + __logf(l) : -INFINITY;
+  *reinterpret_cast<u32x4*>(a.out + ((int64_t)b * a.H + h) * D_C + ch) = packed;
+  if (cl == 0 && cq == 0) a.lse[(int64_t)b * a.H + h] = l > 0.f ? M + __logf(l) : -INFINITY;
 }
 
 SplitPlan plan_splits(int B, int H, int max_pages) {
@@ -777,13 +782,19 @@ hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream) {
     decode_kernel<2><<<grid, dim3(256), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;  // one range: output written directly
-  const dim3 cgrid(a.B * a.H);
-  if (a.n_split >= 8)
-    combine_kernel<8><<<cgrid, dim3(512), 0, stream>>>(a);
-  else if (a.n_split >= 4)
-    combine_kernel<4><<<cgrid, dim3(256), 0, stream>>>(a);
-  else
-    combine_kernel<2><<<cgrid, dim3(128), 0, stream>>>(a);
+  // enough workgroups to spread the partials' reads: a row splits into four
+  // channel blocks when there are few rows
+  const int rows = a.B * a.H;
+  if (a.n_split >= 8) {
+    if (rows < 1024)
+      combine_kernel<8, 16><<<dim3(rows * 4), dim3(128), 0, stream>>>(a);
+    else
+      combine_kernel<8, 64><<<dim3(rows), dim3(512), 0, stream>>>(a);
+  } else if (a.n_split >= 4) {
+    combine_kernel<4, 64><<<dim3(rows), dim3(256), 0, stream>>>(a);
+  } else {
+    combine_kernel<2, 64><<<dim3(rows), dim3(128), 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
