@@ -81,6 +81,52 @@ def test_decode_edge_lengths(c_bits, H):
     assert torch.isneginf(lse[b0]).all()
 
 
+def test_decode_single_range_writes_output_directly():
+    """With enough sequences x head blocks to fill the GPU (64 x 8) and short
+    page tables, each sequence is one page range: the decode writes out / lse
+    itself and no combine runs."""
+    cfg = _cfg(4)
+    lens = [(37 * b) % 300 + 1 for b in range(64)]
+    inp = synth.build_cache_inputs(lens, 128, seed=61, device="cpu")
+    # one range per sequence: the workspace holds a single partial per (b, h)
+    assert mla.decode_workspace_bytes(cfg, 64, 128, inp.page_table.shape[1]) == 64 * 128 * 1028
+    print("[case] decode single range B64 H128", flush=True)
+    pages, sink, local = gpu_cache(cfg, inp, len(lens))
+    out, lse = gpu_decode(cfg, inp, pages, sink, local)
+    torch.cuda.synchronize()
+    oc = ocfg_of(cfg)
+    op, osink, olocal = oracle_cache(oc, inp, len(lens))
+    ref, ref_lse = oracle_decode(oc, inp, op, osink, olocal, synth.SOFTMAX_SCALE)
+    assert_decode_ok(out, lse, ref, ref_lse, label="single range")
+
+
+def test_decode_rescales_when_scores_jump():
+    """Keys of later tokens scaled up so their scores exceed the running
+    reference max by far more than the lazy-rescale threshold mid-sequence
+    (and inside one page range): the shared max moves, O and l are rescaled."""
+    cfg = _cfg(4)
+    lens = [3000, 700]
+    inp = synth.build_cache_inputs(lens, 16, seed=23, device="cpu")
+    c = inp.c_kv.float()
+    k = inp.k_rope.float()
+    # tokens 1500.. of sequence 0 and 400.. of sequence 1 (packed and window)
+    big = torch.zeros(c.shape[0], dtype=torch.bool)
+    big[1500:3000] = True
+    big[3000 + 400:] = True
+    c[big] *= 12.0
+    k[big] *= 12.0
+    inp.c_kv = c.to(torch.bfloat16)
+    inp.k_rope = k.to(torch.bfloat16)
+    print("[case] decode score jumps", flush=True)
+    pages, sink, local = gpu_cache(cfg, inp, len(lens))
+    out, lse = gpu_decode(cfg, inp, pages, sink, local)
+    torch.cuda.synchronize()
+    oc = ocfg_of(cfg)
+    op, osink, olocal = oracle_cache(oc, inp, len(lens))
+    ref, ref_lse = oracle_decode(oc, inp, op, osink, olocal, synth.SOFTMAX_SCALE)
+    assert_decode_ok(out, lse, ref, ref_lse, label="score jumps")
+
+
 def test_decode_tiny_workload():
     wl = synth.WORKLOADS["tiny"]
     cfg = _cfg(wl.c_bits)
