@@ -671,10 +671,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 // Merge the page-range partials of one (sequence, head): lse = log sum
 // exp(lse_s), out = sum_s exp(lse_s - lse) * o_s. A workgroup takes SL split
 // lanes x CL channel lanes of 8 channels (64 / CL workgroups per row). Each
-// split lane issues the loads of up to eight of its ranges together and folds
-// them with a running max (empty ranges, lse = -inf, hold no output); the SL
-// states are then merged in LDS.
-template <int SL, int CL>
+// split lane issues the loads of U of its ranges together and folds them with
+// a running max (empty ranges, lse = -inf, hold no output); the SL states are
+// then merged in LDS.
+template <int SL, int CL, int U>
 __global__ __launch_bounds__(SL * CL) void combine_kernel(DecodeArgs a) {
   __shared__ float part[SL][8][CL];
   __shared__ float pm[SL], pl[SL];
@@ -690,18 +690,18 @@ __global__ __launch_bounds__(SL * CL) void combine_kernel(DecodeArgs a) {
 
   float m = -INFINITY, l = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = sl; s0 < ns; s0 += 8 * SL) {
-    float ls[8];
-    half8 o[8];
+  for (int s0 = sl; s0 < ns; s0 += U * SL) {
+    float ls[U];
+    half8 o[U];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int s = min(s0 + SL * u, ns - 1);
       ls[u] = s0 + SL * u < ns ? lses[(int64_t)s * a.H] : -INFINITY;
       o[u] = *reinterpret_cast<const half8*>(base + (int64_t)s * stride);
     }
     float mc = ls[0];
 #pragma unroll
-    for (int u = 1; u < 8; ++u) mc = fmaxf(mc, ls[u]);
+    for (int u = 1; u < U; ++u) mc = fmaxf(mc, ls[u]);
     if (mc == -INFINITY) continue;
     const float m_new = fmaxf(m, mc);
     const float r = __expf(m - m_new);  // 0 while m = -inf
@@ -709,7 +709,7 @@ __global__ __launch_bounds__(SL * CL) void combine_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= r;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < U; ++u) {
       const bool ok = ls[u] != -INFINITY;
       const float f = ok ? __expf(ls[u] - m_new) : 0.f;
       l += f;
@@ -782,18 +782,27 @@ hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream) {
     decode_kernel<2><<<grid, dim3(256), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;  // one range: output written directly
-  // enough workgroups to spread the partials' reads: a row splits into four
-  // channel blocks when there are few rows
-  const int rows = a.B * a.H;
-  if (a.n_split >= 8) {
-    if (rows < 1024)
-      combine_kernel<8, 16><<<dim3(rows * 4), dim3(128), 0, stream>>>(a);
-    else
-      combine_kernel<8, 64><<<dim3(rows), dim3(512), 0, stream>>>(a);
-  } else if (a.n_split >= 4) {
-    combine_kernel<4, 64><<<dim3(rows), dim3(256), 0, stream>>>(a);
+  // SL split lanes with U ranges each per round of loads (U covers a lane's
+  // share up to 8); a row splits into four channel blocks when rows are few
+  const int rows = a.B * a.H, ns = a.n_split;
+  const dim3 g1(rows), g4(rows * 4);
+  if (ns >= 8) {
+    const int per = (ns + 7) / 8;
+    if (rows < 1024) {
+      if (per > 4) combine_kernel<8, 16, 8><<<g4, dim3(128), 0, stream>>>(a);
+      else if (per > 2) combine_kernel<8, 16, 4><<<g4, dim3(128), 0, stream>>>(a);
+      else if (per > 1) combine_kernel<8, 16, 2><<<g4, dim3(128), 0, stream>>>(a);
+      else combine_kernel<8, 16, 1><<<g4, dim3(128), 0, stream>>>(a);
+    } else {
+      if (per > 4) combine_kernel<8, 64, 8><<<g1, dim3(512), 0, stream>>>(a);
+      else if (per > 2) combine_kernel<8, 64, 4><<<g1, dim3(512), 0, stream>>>(a);
+      else if (per > 1) combine_kernel<8, 64, 2><<<g1, dim3(512), 0, stream>>>(a);
+      else combine_kernel<8, 64, 1><<<g1, dim3(512), 0, stream>>>(a);
+    }
+  } else if (ns >= 4) {
+    combine_kernel<4, 64, 2><<<g1, dim3(256), 0, stream>>>(a);
   } else {
-    combine_kernel<2, 64><<<dim3(rows), dim3(128), 0, stream>>>(a);
+    combine_kernel<2, 64, 2><<<g1, dim3(128), 0, stream>>>(a);
   }
   return hipGetLastError();
 }
