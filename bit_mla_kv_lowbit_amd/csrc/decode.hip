@@ -28,10 +28,11 @@
 //      by more than 2^8 (then the wave uses its own page max, publishes it, and
 //      every wave rescales by the same factors after the barrier), so P stays
 //      below 256 in fp16 and in the common case nothing is rescaled;
-//   4. after the page's one barrier, wave w accumulates O^T for its channels:
-//      V^T and P^T are read transposed from LDS with ds_read_b64_tr_b16.
-// The PV product of one page runs inside the score loop of the next one. The
-// partials (O / l, log-sum-exp) of the workgroups of a sequence are merged by
+//   4. after the page's barrier, wave w accumulates O^T for its channels:
+//      V^T and P^T are read transposed from LDS with ds_read_b64_tr_b16; a
+//      second barrier frees the tile for the next page.
+// Two workgroups share each CU, so one's PV product and barriers overlap the
+// other's score loop. The partials (O / l, log-sum-exp) of the workgroups of a sequence are merged by
 // combine_kernel (split-K over the sequence with an LSE combine: one global
 // softmax); a sequence with a single page range writes its output directly.
 #include "mla_common.h"
@@ -225,9 +226,7 @@ __device__ __forceinline__ half8 pv_load(const PvCtx& c, int i, int w, int j, in
 }
 
 // O^T[16 channels, block mb of wave w x 16 heads] += V^T P^T over the 32 tokens
-// of K-block kb (step i = 2 mb + kb), after issuing the reads of step i + 1. The
-// sixteen steps are issued one per content group from inside the next page's
-// score loop.
+// of K-block kb (step i = 2 mb + kb), after issuing the reads of step i + 1.
 __device__ __forceinline__ void pv_step(AttnState& st, PvCtx& c, int i, int w, int j, int t16) {
   const half8 cur = c.av;
   if (i + 1 < 16) c.av = pv_load(c, i + 1, w, j, t16);
@@ -428,6 +427,38 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
+// Page range [it0, it0 + n_it) of workgroup `split` (of n_split) of a
+// sequence of L tokens. Pages with protected tokens cost about twice a packed
+// page (their BF16 rows are read when they are scored), so the boundaries
+// balance the weight c(i) of pages 0 .. i - 1: one per page, plus one for the
+// sink page and for each page from the one holding the window's first token.
+// Split s starts at the smallest i with c(i) >= s * W / n_split.
+struct PageRange {
+  int it0, n_it;
+};
+__device__ __forceinline__ PageRange page_range(int L, int n_sink, int n_local, int split,
+                                                int n_split) {
+  const int n_s = min(n_sink, L);
+  const int lo_start = max(n_sink, L - n_local);  // first token of the recent window
+  const int n_items = (L + PAGE - 1) / PAGE;
+  const int wp = min(lo_start / PAGE, n_items);
+  const int sink_w = n_s > 0 ? 1 : 0;
+  auto weight_before = [&](int i) { return i + sink_w * min(i, 1) + max(0, i - wp); };
+  const int64_t W = weight_before(n_items);
+  auto first_item = [&](int s) {
+    int lo_i = 0, hi_i = n_items;
+    while (lo_i < hi_i) {
+      const int mid = (lo_i + hi_i) >> 1;
+      if ((int64_t)weight_before(mid) * n_split >= (int64_t)s * W) hi_i = mid;
+      else lo_i = mid + 1;
+    }
+    return lo_i;
+  };
+  const int i0 = first_item(split);
+  const int i1 = first_item(split + 1);  // i1 - i0 <= MAX_ITEMS by the split plan
+  return {i0, i1 - i0};
+}
+
 // Work items of a sequence: its pages (protected tokens taken from the BF16
 // buffers in their own slots). Workgroup `split` takes a contiguous range of
 // the pages (an even share of their cost), and writes one partial (O / l,
@@ -471,6 +502,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   const int row = 16 * w + t16;  // token row of this lane in the page / tile
   const int h = hb * 16 + t16;
 
+  // This workgroup's page range. The length arrives one round trip after the
+  // arguments, and the page table one more after it; so the range is first
+  // computed for a sequence that fills its page-table row (the common case of
+  // a batch of equal lengths) and its page ids are read at once, while the
+  // length and Q are in flight. A range that turns out different is read
+  // again.
+  const int L_raw = *(volatile const_i32*)(seq_lens + b);  // volatile: issued first
+
   // Q of the 16 heads is read once per workgroup (16 B per thread and chunk)
   // and staged in the tile (rows of QS halves) before the waves take their
   // operands from it.
@@ -487,49 +526,36 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                                                         : qr + hh * D_R + 8 * (k - D_C / 8));
     }
   }
+  const int Lg = max_pages * PAGE;
+  const int* ptab_b = page_table + (int64_t)b * max_pages;
+  const PageRange rg = page_range(Lg, n_sink, n_local, split, n_split);
+  const int pid0_g = rg.n_it > 0 ? *(const_i32*)(ptab_b + rg.it0) : 0;
+  const int pidm_g = tid < rg.n_it ? ptab_b[rg.it0 + tid] : 0;
 
   // lengths are clamped to what the page table can hold
-  const int L = min(max(*(const_i32*)(seq_lens + b), 0), max_pages * PAGE);
+  const int L = min(max(L_raw, 0), Lg);
   const float sl2 = a.scale_log2;
-
-  // Items of this sequence: its pages. Token p of a page is taken from the
-  // packed codes, or from the BF16 buffers if it is protected (p < n_sink:
-  // sink; p >= lo_start: the recent window, ring slot p mod n_local), or is
-  // masked if p >= L.
+  const PageRange rr = L == Lg ? rg : page_range(L, n_sink, n_local, split, n_split);
+  const int it0 = rr.it0;
+  const int n_it = rr.n_it;
+  const int n_pk = n_it;  // every item is a page of the page table
+  // Token p of a page is taken from the packed codes, or from the BF16 buffers
+  // if it is protected (p < n_s: sink; p >= lo_start: the recent window, ring
+  // slot p mod n_local), or is masked if p >= L.
   const int n_s = min(n_sink, L);
   const int lo_start = max(n_sink, L - n_local);  // first token of the recent window
-  const int n_items = (L + PAGE - 1) / PAGE;
-  // Pages with protected tokens cost about twice a packed page (their BF16
-  // rows are read when they are scored), so the split boundaries balance
-  // the weight c(i) of pages 0 .. i - 1: one per page, plus one for the sink
-  // page and for each page from the one holding the window's first token.
-  const int wp = min(lo_start / PAGE, n_items);
-  const int sink_w = n_s > 0 ? 1 : 0;
-  auto weight_before = [&](int i) { return i + sink_w * min(i, 1) + max(0, i - wp); };
-  const int64_t W = weight_before(n_items);
-  auto first_item = [&](int s) {  // smallest i with c(i) >= s * W / n_split
-    int lo_i = 0, hi_i = n_items;
-    while (lo_i < hi_i) {
-      const int mid = (lo_i + hi_i) >> 1;
-      if ((int64_t)weight_before(mid) * n_split >= (int64_t)s * W) hi_i = mid;
-      else lo_i = mid + 1;
-    }
-    return lo_i;
-  };
-  const int it0 = first_item(split);
-  const int it1 = first_item(split + 1);  // it1 - it0 <= MAX_ITEMS by the split plan
-  const int n_it = it1 - it0;
-  const int n_pk = n_it;  // every item is a page of the page table
+  int pid0 = pid0_g, pid_mine = pidm_g;
+  if (rr.it0 != rg.it0 || rr.n_it != rg.n_it) {
+    pid0 = n_pk > 0 ? *(const_i32*)(ptab_b + it0) : 0;
+    pid_mine = tid < n_pk ? ptab_b[it0 + tid] : 0;
+  }
 
-  // This workgroup's page ids, and the first page, which stays in flight
-  // while Q is converted. Loads past the last item repeat it; with no item
-  // the descriptor has an empty range (loads return 0, touch nothing), so
-  // the loads stay unconditional and the wait counts static.
-  const int* ptab = page_table + (int64_t)b * max_pages + it0;
-  const int pid_mine = tid < n_pk ? ptab[tid] : 0;
+  // The first page stays in flight while Q is converted. Loads past the last
+  // item repeat it; with no item the descriptor has an empty range (loads
+  // return 0, touch nothing), so the loads stay unconditional and the wait
+  // counts static.
   const LaneOffsets<CB> lo(row, j);
   PageRegs<CB> regs;
-  const int pid0 = n_pk > 0 ? *(const_i32*)ptab : 0;
   load_page<CB>(regs, page_rsrc<CB>(a.pages, pid0, n_pk > 0), lo);
 #pragma unroll
   for (int i = 0; i < (NCH + 255) / 256; ++i) {
@@ -538,18 +564,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();  // Q staged
 
-  // Q as the A operand of the 18 groups (lane = head t16; channels 8j .. 8j + 7
-  // of each group), and the z-term A operands (see packed_scores).
+  // Q as fp16 A operands, and the z-term A operands (see packed_scores).
   half8 qA[NG_C + NG_R];
   half8 qz1, qz2;
   {
+    // group sums Q_g of head t16: one MFMA with a ones A operand (Q as the B
+    // operand has the same lane layout as the A operand)
+    float qs[NG_C + NG_R];
     u32x4 qraw[NG_C + NG_R];
 #pragma unroll
     for (int g = 0; g < NG_C + NG_R; ++g)
       qraw[g] = *reinterpret_cast<const u32x4*>(tile + t16 * QS + group_channel(g, j));
-    // group sums Q_g of head t16: one MFMA with a ones A operand (Q as the B
-    // operand has the same lane layout as the A operand)
-    float qs[NG_C + NG_R];
     const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
     const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -590,6 +615,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     float4v S = packed_scores<CB>(t, qA, qz1, qz2, tile, row, j);
     if (mixed) {
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);  // pages with BF16 rows are the slow ones
       const uint64_t pm = __builtin_amdgcn_ballot_w64(prot);
       if (pm != 0) {
         // lanes without a protected token read the first protected lane's row
@@ -615,6 +641,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     for (int k = 0;; ++k) {
       const int pid_next = pids[max(0, min(k + 1, n_pk - 1))];  // read ahead of its use
       const float4v S = score_item(regs, k);
+      // From the softmax to the end of the PV product the wave's instructions
+      // take precedence over those of the other workgroup's wave on the SIMD
+      // (its score loop), so the short, latency-bound stretches around the
+      // barrier do not wait behind a long run of VALU work.
+      __builtin_amdgcn_s_setprio(2);
       softmax_tokens(st, S, pl, sl2, w, lane, row, j, t16);
       load_page<CB>(regs, page_rsrc<CB>(a.pages, n_pk > 0 ? __builtin_amdgcn_readfirstlane(pid_next) : 0,
                                         n_pk > 0), lo);
@@ -623,6 +654,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       pv_begin(pv, st, tile, pl, w, j, t16);
 #pragma unroll
       for (int i = 0; i < 16; ++i) pv_step(st, pv, i, w, j, t16);
+      __builtin_amdgcn_s_setprio(0);
       if (k + 1 >= n_it) break;
       __syncthreads();
     }
