@@ -510,9 +510,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   // again.
   const int L_raw = *(volatile const_i32*)(seq_lens + b);  // volatile: issued first
 
-  // Q of the 16 heads is read once per workgroup (16 B per thread and chunk)
-  // and staged in the tile (rows of QS halves) before the waves take their
-  // operands from it.
+  // Q of the 16 heads is read once per workgroup (16 B per thread and chunk),
+  // converted to fp16 and staged in the tile (rows of QS halves) before the
+  // waves take their operands from it.
   constexpr int QS = D_ALL + 8;
   constexpr int NCH = 16 * (D_ALL / 8);  // 8-channel chunks
   u32x4 qv[(NCH + 255) / 256];
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < (NCH + 255) / 256; ++i) {
     const int c = tid + 256 * i, hh = c / (D_ALL / 8), k = c % (D_ALL / 8);
-    if (c < NCH) *reinterpret_cast<u32x4*>(tile + hh * QS + 8 * k) = qv[i];
+    if (c < NCH) *reinterpret_cast<half8*>(tile + hh * QS + 8 * k) = bf16x8_to_f16x8(qv[i]);
   }
   __syncthreads();  // Q staged
 
@@ -571,17 +571,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     // group sums Q_g of head t16: one MFMA with a ones A operand (Q as the B
     // operand has the same lane layout as the A operand)
     float qs[NG_C + NG_R];
-    u32x4 qraw[NG_C + NG_R];
 #pragma unroll
     for (int g = 0; g < NG_C + NG_R; ++g)
-      qraw[g] = *reinterpret_cast<const u32x4*>(tile + t16 * QS + group_channel(g, j));
+      qA[g] = *reinterpret_cast<const half8*>(tile + t16 * QS + group_channel(g, j));
     const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
     const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int g = 0; g < NG_C + NG_R; ++g) {
-      qA[g] = bf16x8_to_f16x8(qraw[g]);
+    for (int g = 0; g < NG_C + NG_R; ++g)
       qs[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, qA[g], zero4, 0, 0, 0)[0];
-    }
     const bool lo_part = (j & 1) != 0, lowj = j < 2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
