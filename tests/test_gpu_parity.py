@@ -81,6 +81,27 @@ def test_decode_edge_lengths(c_bits, H):
     assert torch.isneginf(lse[b0]).all()
 
 
+@pytest.mark.parametrize("c_bits,H", [(4, 16), (2, 16), (4, 128)])
+def test_decode_full_and_short_rows_in_one_batch(c_bits, H):
+    """Sequences that fill their page-table row next to shorter ones: the
+    decode first reads the page ids of the range a full row would give and
+    reads them again when the length says otherwise, so both cases (and an
+    empty sequence) meet in one launch."""
+    lens = [4096, 4000, 4096, 64, 4033, 4096, 0, 4095]
+    cfg = _cfg(c_bits)
+    inp = synth.build_cache_inputs(lens, H, seed=77 + H + c_bits, device="cpu")
+    assert inp.page_table.shape[1] * 64 == max(lens)
+    print(f"[case] decode full/short rows c_bits={c_bits} H={H}", flush=True)
+    pages, sink, local = gpu_cache(cfg, inp, len(lens))
+    out, lse = gpu_decode(cfg, inp, pages, sink, local)
+    torch.cuda.synchronize()
+    oc = ocfg_of(cfg)
+    op, osink, olocal = oracle_cache(oc, inp, len(lens))
+    ref, ref_lse = oracle_decode(oc, inp, op, osink, olocal, synth.SOFTMAX_SCALE)
+    assert_decode_ok(out, lse, ref, ref_lse, label=f"full/short rows c{c_bits} H{H}")
+    assert torch.isneginf(lse[lens.index(0)]).all()
+
+
 def test_decode_single_range_writes_output_directly():
     """With enough sequences x head blocks to fill the GPU (64 x 8) and short
     page tables, each sequence is one page range: the decode writes out / lse
