@@ -88,6 +88,14 @@ def lib():
         L.orc_decode.restype = i32
         L.orc_combine.argtypes = [i32, i32, P, P, P, P]
         L.orc_combine.restype = None
+        L.orc_bf16_page_bytes.argtypes = [P]
+        L.orc_bf16_page_bytes.restype = ctypes.c_size_t
+        L.orc_bf16_write.argtypes = [P, i32, P, P, P, P, P, i32, i32, P, ctypes.c_int64]
+        L.orc_bf16_write.restype = i32
+        L.orc_bf16_decode.argtypes = [P, i32, i32, f64, P, P, P, P, i32, P, i32, P, P, P, P]
+        L.orc_bf16_decode.restype = i32
+        L.orc_qdq.argtypes = [P, i32, P, P, P, P]
+        L.orc_qdq.restype = i32
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = i32
         _lib = L
@@ -226,3 +234,60 @@ def combine(o_s, lse_s):
     lse = np.zeros(1, np.float64)
     lib().orc_combine(n, d, _p(o_s), _p(lse_s), _p(out), _p(lse))
     return out, float(lse[0])
+
+
+def _sel(B: int, H: int, sel):
+    if sel is None:
+        return 0, np.zeros(1, np.int32), np.zeros(1, np.int32), B * H
+    sel = np.asarray(sel, dtype=np.int32).reshape(-1, 2)
+    return sel.shape[0], _i32(sel[:, 0]), _i32(sel[:, 1]), sel.shape[0]
+
+
+def bf16_page_bytes(cfg: Cfg) -> int:
+    c = cfg.c()
+    return int(lib().orc_bf16_page_bytes(ctypes.byref(c)))
+
+
+def bf16_write(cfg: Cfg, c_kv, k_rope, seq_idx, pos, page_table, pages: np.ndarray) -> None:
+    """Copy token rows into a BF16 paged cache (pages uint16 [num_pages, page_size,
+    d_c + d_r]), in place."""
+    c = cfg.c()
+    c_kv, k_rope = _u16(c_kv), _u16(k_rope)
+    seq_idx, pos, page_table = map(_i32, (seq_idx, pos, page_table))
+    B, max_pages = page_table.shape
+    assert pages.dtype == np.uint16 and pages.flags["C_CONTIGUOUS"]
+    rc = lib().orc_bf16_write(ctypes.byref(c), int(seq_idx.size), _p(c_kv), _p(k_rope),
+                              _p(seq_idx), _p(pos), _p(page_table), B, max_pages, _p(pages),
+                              pages.shape[0])
+    if rc != 0:
+        raise ValueError(f"orc_bf16_write rejected its arguments ({rc})")
+
+
+def bf16_decode(cfg: Cfg, scale: float, q_lat, q_rope, pages, page_table, seq_lens, sel=None):
+    """fp64 attention over a BF16 paged cache. Returns (out [rows, d_c], lse [rows])."""
+    c = cfg.c()
+    q_lat, q_rope = _u16(q_lat), _u16(q_rope)
+    B, H = q_lat.shape[0], q_lat.shape[1]
+    page_table, seq_lens = _i32(page_table), _i32(seq_lens)
+    n_sel, sb, sh, rows = _sel(B, H, sel)
+    out = np.zeros((rows, cfg.d_c), np.float64)
+    lse = np.zeros(rows, np.float64)
+    rc = lib().orc_bf16_decode(ctypes.byref(c), B, H, float(scale), _p(q_lat), _p(q_rope),
+                               _p(_u16(pages)), _p(page_table), page_table.shape[1],
+                               _p(seq_lens), n_sel, _p(sb), _p(sh), _p(out), _p(lse))
+    if rc != 0:
+        raise ValueError(f"orc_bf16_decode rejected its arguments ({rc})")
+    return out, lse
+
+
+def qdq(cfg: Cfg, c_kv, k_rope):
+    """Simulated quantize-dequantize of token rows; returns bf16 bits (out_c, out_r)."""
+    c = cfg.c()
+    c_kv, k_rope = _u16(c_kv), _u16(k_rope)
+    n = c_kv.shape[0]
+    out_c = np.zeros((n, cfg.d_c), np.uint16)
+    out_r = np.zeros((n, cfg.d_r), np.uint16)
+    rc = lib().orc_qdq(ctypes.byref(c), n, _p(c_kv), _p(k_rope), _p(out_c), _p(out_r))
+    if rc != 0:
+        raise ValueError(f"orc_qdq rejected its arguments ({rc})")
+    return out_c, out_r

@@ -459,3 +459,118 @@ void orc_combine(int n, int d, const double* o_s, const double* lse_s, double* o
     for (int i = 0; i < d; ++i) out[i] += w * o_s[(size_t)s * d + i];
   }
 }
+
+/* ---------------- paired BF16 cache (the baseline of Figure 5(b), Table 9) ----------------
+ *
+ * The unquantized cache that the low-bit kernel is measured against keeps
+ * every token's [c | k_rope] row in BF16. Reading taken here (the pages name
+ * the baseline but not its layout): the same paging as the packed cache, one
+ * page = page_size rows of d_c + d_r bf16 values, row = slot = p mod
+ * page_size, page = page_table[b][p div page_size]; no protected buffers. */
+
+size_t orc_bf16_page_bytes(const orc_cfg* c) {
+  return (size_t)c->page_size * (size_t)(c->d_c + c->d_r) * 2u;
+}
+
+int orc_bf16_write(const orc_cfg* c, int n, const uint16_t* c_kv, const uint16_t* k_rope,
+                   const int32_t* seq_idx, const int32_t* pos, const int32_t* page_table,
+                   int B, int max_pages, uint16_t* pages, int64_t num_pages) {
+  if (orc_check_cfg(c)) return -1;
+  const int D = c->d_c + c->d_r;
+  for (int t = 0; t < n; ++t) {
+    int b = seq_idx[t], p = pos[t];
+    if (b < 0 || b >= B || p < 0 || p >= max_pages * c->page_size) return -1;
+    int64_t page = page_table[(size_t)b * max_pages + p / c->page_size];
+    if (page < 0 || page >= num_pages) return -1;
+    uint16_t* row = pages + ((size_t)page * c->page_size + p % c->page_size) * D;
+    for (int i = 0; i < c->d_c; ++i) row[i] = c_kv[(size_t)t * c->d_c + i];
+    for (int i = 0; i < c->d_r; ++i) row[c->d_c + i] = k_rope[(size_t)t * c->d_r + i];
+  }
+  return 0;
+}
+
+/* Exact attention (fp64) of each selected (b, h) over the bf16 rows of tokens
+ * [0, seq_lens[b]); same row selection and outputs as orc_decode. */
+int orc_bf16_decode(const orc_cfg* c, int B, int H, double scale, const uint16_t* q_lat,
+                    const uint16_t* q_rope, const uint16_t* pages, const int32_t* page_table,
+                    int max_pages, const int32_t* seq_lens, int n_sel, const int32_t* sel_b,
+                    const int32_t* sel_h, double* out, double* lse) {
+  if (orc_check_cfg(c)) return -1;
+  const int D = c->d_c + c->d_r;
+  const int n_rows = n_sel > 0 ? n_sel : B * H;
+  for (int b = 0; b < B; ++b) {
+    int cnt = 0;
+    for (int r = 0; r < n_rows; ++r)
+      if ((n_sel > 0 ? sel_b[r] : r / H) == b) cnt++;
+    if (cnt == 0) continue;
+    const int n = seq_lens[b] > 0 ? seq_lens[b] : 0;
+    if (n > max_pages * c->page_size) return -1;
+    double* kc = (double*)malloc(sizeof(double) * ((size_t)n * c->d_c + 1));
+    double* kr = (double*)malloc(sizeof(double) * ((size_t)n * c->d_r + 1));
+    if (!kc || !kr) {
+      free(kc);
+      free(kr);
+      return -2;
+    }
+    for (int p = 0; p < n; ++p) {
+      int64_t page = page_table[(size_t)b * max_pages + p / c->page_size];
+      const uint16_t* row = pages + ((size_t)page * c->page_size + p % c->page_size) * D;
+      for (int i = 0; i < c->d_c; ++i) kc[(size_t)p * c->d_c + i] = orc_bf16_to_f32(row[i]);
+      for (int i = 0; i < c->d_r; ++i)
+        kr[(size_t)p * c->d_r + i] = orc_bf16_to_f32(row[c->d_c + i]);
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < n_rows; ++r) {
+      int rb = n_sel > 0 ? sel_b[r] : r / H;
+      if (rb != b) continue;
+      int h = n_sel > 0 ? sel_h[r] : r % H;
+      double ql[1024], qr[1024];
+      for (int i = 0; i < c->d_c; ++i)
+        ql[i] = orc_bf16_to_f32(q_lat[((size_t)b * H + h) * c->d_c + i]);
+      for (int i = 0; i < c->d_r; ++i)
+        qr[i] = orc_bf16_to_f32(q_rope[((size_t)b * H + h) * c->d_r + i]);
+      double* score = (double*)malloc(sizeof(double) * ((size_t)n + 1));
+      attend(n, c->d_c, c->d_r, scale, ql, qr, kc, kr, score, out + (size_t)r * c->d_c,
+             lse + r);
+      free(score);
+    }
+    free(kc);
+    free(kr);
+  }
+  return 0;
+}
+
+/* ---------------- simulated quantize-dequantize (QDQ, Figure 3 caption) ----------------
+ *
+ * Each group of each token row goes through the writer's quantizer (readings
+ * Q1-Q3) and comes back as x^ = q * s16 + z16. Reading taken here: that value
+ * is rounded to fp32 (nearest even; it is exact in fp64) and then to bf16
+ * (nearest even), the precision of the input rows. */
+static uint16_t dequant_bf16(uint8_t q, uint16_t s16, uint16_t z16) {
+  double v = (double)q * orc_f16_to_f64(s16) + orc_f16_to_f64(z16); /* exact */
+  volatile float f = (float)v; /* nearest even */
+  return orc_f64_to_bf16((double)f);
+}
+
+static void qdq_vector(const uint16_t* in, int d, int bits, int group, uint16_t* out) {
+  float x[1024];
+  uint8_t q[1024];
+  for (int g = 0; g < d / group; ++g) {
+    uint16_t s16, z16;
+    for (int i = 0; i < group; ++i) x[i] = orc_bf16_to_f32(in[g * group + i]);
+    orc_quantize_group(x, group, bits, &s16, &z16, q);
+    for (int i = 0; i < group; ++i) out[g * group + i] = dequant_bf16(q[i], s16, z16);
+  }
+}
+
+int orc_qdq(const orc_cfg* c, int n, const uint16_t* c_kv, const uint16_t* k_rope,
+            uint16_t* out_c, uint16_t* out_r) {
+  if (orc_check_cfg(c)) return -1;
+  for (int t = 0; t < n; ++t) {
+    qdq_vector(c_kv + (size_t)t * c->d_c, c->d_c, c->c_bits, c->group,
+               out_c + (size_t)t * c->d_c);
+    qdq_vector(k_rope + (size_t)t * c->d_r, c->d_r, c->r_bits, c->group,
+               out_r + (size_t)t * c->d_r);
+  }
+  return 0;
+}

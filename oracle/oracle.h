@@ -96,6 +96,30 @@ int orc_decode(const orc_cfg* cfg, int B, int H, double scale, const uint16_t* q
 /* Merge n partial results (o_s[n][d], lse_s[n]) of one row into (out, lse). */
 void orc_combine(int n, int d, const double* o_s, const double* lse_s, double* out, double* lse);
 
+/* Paired BF16 cache, the unquantized baseline the low-bit kernel is measured
+ * against (Figure 5(b) caption, Table 9 caption). Page = page_size rows of
+ * [c (d_c) | k_rope (d_r)] bf16; row = slot of the token. */
+size_t orc_bf16_page_bytes(const orc_cfg* cfg);
+/* Copy each token's row into its page slot. Returns 0, or -1 on an index out
+ * of range. */
+int orc_bf16_write(const orc_cfg* cfg, int n_tokens, const uint16_t* c_kv,
+                   const uint16_t* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                   const int32_t* page_table, int B, int max_pages, uint16_t* pages,
+                   int64_t num_pages);
+/* Exact (fp64) attention over tokens [0, seq_lens[b]) of the BF16 cache; row
+ * selection and outputs as in orc_decode. */
+int orc_bf16_decode(const orc_cfg* cfg, int B, int H, double scale, const uint16_t* q_lat,
+                    const uint16_t* q_rope, const uint16_t* pages, const int32_t* page_table,
+                    int max_pages, const int32_t* seq_lens, int n_sel, const int32_t* sel_b,
+                    const int32_t* sel_h, double* out, double* lse);
+
+/* Simulated quantize-dequantize (QDQ, Figure 3 caption): every group of every
+ * token row through the writer's quantizer and back, x^ = q * s16 + z16,
+ * rounded to fp32 and then to bf16 (both nearest even). out_c [n][d_c] and
+ * out_r [n][d_r] are bf16 bit patterns. Returns 0 or -1. */
+int orc_qdq(const orc_cfg* cfg, int n_tokens, const uint16_t* c_kv, const uint16_t* k_rope,
+            uint16_t* out_c, uint16_t* out_r);
+
 /* Threads the oracle's parallel loops use. */
 int orc_num_threads(void);
 
