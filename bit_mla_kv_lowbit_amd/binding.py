@@ -78,6 +78,16 @@ def lib() -> ctypes.CDLL:
         L.mla_lowbit_write_decode.argtypes = [P, i32, i32, ctypes.c_float, P, P, P, P, P, P, P, i32,
                                               P, P, P, P, P, P, sz, P]
         L.mla_lowbit_write_decode.restype = i32
+        L.mla_lowbit_qdq.argtypes = [P, i32, P, P, P, P, P]
+        L.mla_lowbit_qdq.restype = i32
+        L.mla_bf16_page_bytes.argtypes = []
+        L.mla_bf16_page_bytes.restype = sz
+        L.mla_bf16_decode_workspace_bytes.argtypes = [i32, i32, i32]
+        L.mla_bf16_decode_workspace_bytes.restype = sz
+        L.mla_bf16_write.argtypes = [i32, P, P, P, P, P, i32, i32, P, P]
+        L.mla_bf16_write.restype = i32
+        L.mla_bf16_decode.argtypes = [i32, i32, ctypes.c_float, P, P, P, P, i32, P, P, P, P, sz, P]
+        L.mla_bf16_decode.restype = i32
         _lib = L
     return _lib
 
@@ -206,4 +216,74 @@ def write_decode(cfg: Config, c_kv, k_rope, pos, q_lat, q_rope, pages, page_tabl
                                        workspace.numel() * workspace.element_size(),
                                        _stream(stream))
     _check("mla_lowbit_write_decode", rc)
+    return out, lse
+
+
+def qdq(cfg: Config, c_kv, k_rope, out_c=None, out_r=None, stream=None):
+    """mla_lowbit_qdq: simulated quantize-dequantize of token rows (bf16 in, bf16 out)."""
+    _want(c_kv, torch.bfloat16, "c_kv")
+    _want(k_rope, torch.bfloat16, "k_rope")
+    n = int(c_kv.shape[0])
+    if c_kv.shape != (n, cfg.d_c) or k_rope.shape != (n, cfg.d_r):
+        raise ValueError("c_kv / k_rope shapes do not match the config")
+    if out_c is None:
+        out_c = torch.empty_like(c_kv)
+    if out_r is None:
+        out_r = torch.empty_like(k_rope)
+    c = cfg.c()
+    rc = lib().mla_lowbit_qdq(ctypes.byref(c), n, _ptr(c_kv), _ptr(k_rope), _ptr(out_c),
+                              _ptr(out_r), _stream(stream))
+    _check("mla_lowbit_qdq", rc)
+    return out_c, out_r
+
+
+def bf16_page_bytes() -> int:
+    return int(lib().mla_bf16_page_bytes())
+
+
+def bf16_decode_workspace_bytes(B: int, H: int, max_pages: int) -> int:
+    return int(lib().mla_bf16_decode_workspace_bytes(B, H, max_pages))
+
+
+def allocate_bf16_cache(num_pages: int, device="cuda", d_c: int = 512, d_r: int = 64,
+                        page_size: int = 64):
+    """Zeroed BF16 paged cache: bf16 [num_pages, page_size, d_c + d_r]."""
+    return torch.zeros(num_pages, page_size, d_c + d_r, dtype=torch.bfloat16, device=device)
+
+
+def bf16_write(c_kv, k_rope, seq_idx, pos, page_table, pages, stream=None) -> None:
+    """mla_bf16_write: copy token rows into the BF16 paged cache."""
+    _want(c_kv, torch.bfloat16, "c_kv")
+    _want(k_rope, torch.bfloat16, "k_rope")
+    for n, t in (("seq_idx", seq_idx), ("pos", pos), ("page_table", page_table)):
+        _want(t, torch.int32, n)
+    n = int(seq_idx.numel())
+    if c_kv.shape[0] != n or k_rope.shape[0] != n or pos.numel() != n:
+        raise ValueError("c_kv / k_rope / pos do not match seq_idx")
+    B, max_pages = page_table.shape
+    rc = lib().mla_bf16_write(n, _ptr(c_kv), _ptr(k_rope), _ptr(seq_idx), _ptr(pos),
+                              _ptr(page_table), B, max_pages, _ptr(pages), _stream(stream))
+    _check("mla_bf16_write", rc)
+
+
+def bf16_decode(q_lat, q_rope, pages, page_table, seq_lens, scale: float, out=None, lse=None,
+                workspace=None, stream=None):
+    """mla_bf16_decode. Returns (out bf16 [B,H,512], lse fp32 [B,H])."""
+    _want(q_lat, torch.bfloat16, "q_lat")
+    _want(q_rope, torch.bfloat16, "q_rope")
+    B, H, d_c = q_lat.shape
+    max_pages = page_table.shape[1]
+    dev = q_lat.device
+    if out is None:
+        out = torch.empty(B, H, d_c, dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(bf16_decode_workspace_bytes(B, H, max_pages), 16),
+                                dtype=torch.uint8, device=dev)
+    rc = lib().mla_bf16_decode(B, H, float(scale), _ptr(q_lat), _ptr(q_rope), _ptr(pages),
+                               _ptr(page_table), max_pages, _ptr(seq_lens), _ptr(out), _ptr(lse),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(stream))
+    _check("mla_bf16_decode", rc)
     return out, lse

@@ -198,4 +198,75 @@ int mla_lowbit_write_decode(const mla_lowbit_config* cfg, int B, int H, float so
   return launch_decode(a, cfg->c_bits, s) == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ELAUNCH;
 }
 
+int mla_lowbit_qdq(const mla_lowbit_config* cfg, int n_tokens, const void* c_kv,
+                   const void* k_rope, void* out_c, void* out_r, void* stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (n_tokens < 0) return MLA_LOWBIT_EINVAL;
+  if (n_tokens == 0) return MLA_LOWBIT_OK;
+  if (!ok_ptr(c_kv) || !ok_ptr(k_rope) || !ok_ptr(out_c) || !ok_ptr(out_r))
+    return MLA_LOWBIT_EINVAL;
+  QdqArgs a;
+  a.n_tokens = n_tokens;
+  a.c_kv = static_cast<const uint16_t*>(c_kv);
+  a.k_rope = static_cast<const uint16_t*>(k_rope);
+  a.out_c = static_cast<uint16_t*>(out_c);
+  a.out_r = static_cast<uint16_t*>(out_r);
+  return launch_qdq(a, cfg->c_bits, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_LOWBIT_OK
+             : MLA_LOWBIT_ELAUNCH;
+}
+
+size_t mla_bf16_page_bytes(void) { return (size_t)PageGeom<16>::BYTES; }
+
+size_t mla_bf16_decode_workspace_bytes(int B, int H, int max_pages) {
+  if (B < 0 || H <= 0 || H % 16 != 0 || max_pages < 1) return 0;
+  return decode_workspace_bytes(B, H, max_pages);
+}
+
+int mla_bf16_write(int n_tokens, const void* c_kv, const void* k_rope, const int32_t* seq_idx,
+                   const int32_t* pos, const int32_t* page_table, int B, int max_pages,
+                   void* pages, void* stream) {
+  if (n_tokens < 0 || B < 0 || max_pages < 1) return MLA_LOWBIT_EINVAL;
+  if (n_tokens == 0) return MLA_LOWBIT_OK;
+  if (B == 0) return MLA_LOWBIT_EINVAL;
+  if (!ok_ptr(c_kv) || !ok_ptr(k_rope) || !ok_ptr4(seq_idx) || !ok_ptr4(pos) ||
+      !ok_ptr4(page_table) || !ok_ptr(pages))
+    return MLA_LOWBIT_EINVAL;
+  WriteArgs a = {};
+  a.n_tokens = n_tokens;
+  a.c_kv = static_cast<const uint16_t*>(c_kv);
+  a.k_rope = static_cast<const uint16_t*>(k_rope);
+  a.seq_idx = seq_idx;
+  a.pos = pos;
+  a.page_table = page_table;
+  a.B = B;
+  a.max_pages = max_pages;
+  a.pages = static_cast<uint8_t*>(pages);
+  return launch_write(a, 16, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_LOWBIT_OK
+             : MLA_LOWBIT_ELAUNCH;
+}
+
+int mla_bf16_decode(int B, int H, float softmax_scale, const void* q_lat, const void* q_rope,
+                    const void* pages, const int32_t* page_table, int max_pages,
+                    const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (B < 0 || H <= 0 || H % 16 != 0 || max_pages < 1) return MLA_LOWBIT_EINVAL;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_LOWBIT_EINVAL;
+  if (B == 0) return MLA_LOWBIT_OK;
+  if (!ok_ptr(q_lat) || !ok_ptr(q_rope) || !ok_ptr(pages) || !ok_ptr4(page_table) ||
+      !ok_ptr4(seq_lens) || !ok_ptr(out) || !ok_ptr(lse) || !ok_ptr(workspace))
+    return MLA_LOWBIT_EINVAL;
+  if (plan_splits(B, H, max_pages).n_split > MAX_SPLITS) return MLA_LOWBIT_EUNSUPPORTED;
+  if (workspace_bytes < decode_workspace_bytes(B, H, max_pages)) return MLA_LOWBIT_EWORKSPACE;
+  // no protected buffers: n_sink = n_local = 0
+  mla_lowbit_config cfg = {D_C, D_R, 16, 16, GROUP, PAGE, 0, 0};
+  DecodeArgs a = make_decode_args(&cfg, B, H, softmax_scale, q_lat, q_rope, pages, page_table,
+                                  max_pages, seq_lens, nullptr, nullptr, out, lse, workspace);
+  return launch_decode(a, 16, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_LOWBIT_OK
+             : MLA_LOWBIT_ELAUNCH;
+}
+
 }  // extern "C"

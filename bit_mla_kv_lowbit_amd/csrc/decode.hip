@@ -73,6 +73,12 @@ struct PageRegs {
   u32x2 rsz;                 // RoPE (s, z) words
 };
 
+// BF16 baseline page: sub-block j of each of the token's 18 groups, raw bf16.
+template <>
+struct PageRegs<16> {
+  u32x4 k[NG_C + NG_R];
+};
+
 // Byte offsets, inside a page, of what one lane (slot, sub-block j) loads,
 // relative to the start of each region (the region starts go in the scalar
 // offset of the buffer loads). The content code chunk m (16 bytes at + 64 m)
@@ -91,6 +97,14 @@ struct LaneOffsets {
 
 // Buffer descriptor of one physical page (raw byte addressing, range = page;
 // an empty range makes every load return 0 and touch nothing).
+// BF16 page: sub-block j of group g of the row sits at + 64 g (RoPE groups
+// follow the 16 content groups in the row).
+template <>
+struct LaneOffsets<16> {
+  uint32_t c;
+  __device__ LaneOffsets(int slot, int j) : c(slot * PageGeom<16>::ROW + 16 * j) {}
+};
+
 template <int CB>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* pages, int pid,
                                                             bool any = true) {
@@ -102,6 +116,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* pages
 template <int CB>
 __device__ __forceinline__ void load_page(PageRegs<CB>& t, __amdgpu_buffer_rsrc_t rs,
                                           const LaneOffsets<CB>& o) {
+  if constexpr (CB == 16) {
+#pragma unroll
+    for (int g = 0; g < NG_C + NG_R; ++g)
+      t.k[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.c, 64 * g, 0));
+  } else {
   using G = PageGeom<CB>;
 #pragma unroll
   for (int m = 0; m < (CB == 4 ? 4 : 2); ++m)
@@ -111,6 +130,32 @@ __device__ __forceinline__ void load_page(PageRegs<CB>& t, __amdgpu_buffer_rsrc_
     t.sz[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.s, G::OFF_CS + 16 * m, 0));
   t.r = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.r, G::OFF_RC, 0));
   t.rsz = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.rs, G::OFF_RS, 0));
+  }
+}
+
+// Scores of the BF16 baseline use bf16 MFMA on Q and the rows as stored
+// (bf16 values travel in half8 bit containers). Its PV product stays in fp16
+// like the packed cache's: P in bf16 (8 significant bits) would move outputs
+// by up to 2^-9 of the value spread, too much for outlier channels.
+__device__ __forceinline__ float4v mma_bf16(const half8& a, const half8& b, const float4v& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Eight bf16 (bit patterns) -> fp16. Truncation is exact here: bf16 values in
+// the fp16 normal range fit in 11 significant bits (below it, fp16 subnormals
+// lose at most 2^-24).
+__device__ __forceinline__ half8 bf16x8_to_f16x8_rtz(u32x4 w) {
+  half8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2v h = __builtin_bit_cast(
+        half2v, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[i] << 16),
+                                           __uint_as_float(w[i] & 0xffff0000u)));
+    r[2 * i] = h.x;
+    r[2 * i + 1] = h.y;
+  }
+  return r;
 }
 
 // Exact codes of channels 8j..8j+7 (pairs (0,1) (2,3) (4,5) (6,7)) of one group
@@ -417,6 +462,24 @@ __device__ __forceinline__ float4v bf16_scores(const uint16_t* rowp, bool use,
   return S;
 }
 
+// Scores and tile row of a token of a BF16 page (bf16 MFMA on the stored
+// values, fp16 tile); a row with keep false contributes 0 and leaves a zero
+// tile row.
+__device__ __forceinline__ float4v bf16_page_scores(const PageRegs<16>& t, bool keep,
+                                                    const half8 (&qA)[18], _Float16* tile,
+                                                    int row, int j) {
+  float4v S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < NG_C + NG_R; ++g) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 kv = keep ? t.k[g] : z;
+    S = mma_bf16(qA[g], __builtin_bit_cast(half8, kv), S);
+    if (g < NG_C)
+      *reinterpret_cast<half8*>(tile + row * TS + GROUP * g + 8 * j) = bf16x8_to_f16x8_rtz(kv);
+  }
+  return S;
+}
+
 // Sum over the 16 lanes of a row (DPP butterfly: neighbours, pairs, half-row
 // mirror, row mirror).
 __device__ __forceinline__ float row_sum(float v) {
@@ -560,7 +623,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < (NCH + 255) / 256; ++i) {
     const int c = tid + 256 * i, hh = c / (D_ALL / 8), k = c % (D_ALL / 8);
-    if (c < NCH) *reinterpret_cast<half8*>(tile + hh * QS + 8 * k) = bf16x8_to_f16x8(qv[i]);
+    if (c < NCH)
+      *reinterpret_cast<half8*>(tile + hh * QS + 8 * k) =
+          CB == 16 ? __builtin_bit_cast(half8, qv[i]) : bf16x8_to_f16x8(qv[i]);
   }
   __syncthreads();  // Q staged
 
@@ -574,6 +639,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < NG_C + NG_R; ++g)
       qA[g] = *reinterpret_cast<const half8*>(tile + t16 * QS + group_channel(g, j));
+    if constexpr (CB != 16) {
     const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
     const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -587,6 +653,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       const _Float16 h1 = (_Float16)v1, h2 = (_Float16)v2;
       qz1[i] = lo_part ? (_Float16)(v1 - (float)h1) : h1;
       qz2[i] = lo_part ? (_Float16)(v2 - (float)h2) : h2;
+    }
     }
   }
 
@@ -608,23 +675,30 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     const int p = p0 + row;
     const bool valid = p < L;
     const bool prot = valid && (p < n_s || p >= lo_start);
-    if (mixed) mask_token<CB>(t, valid && !prot);
-    float4v S = packed_scores<CB>(t, qA, qz1, qz2, tile, row, j);
-    if (mixed) {
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(1);  // pages with BF16 rows are the slow ones
-      const uint64_t pm = __builtin_amdgcn_ballot_w64(prot);
-      if (pm != 0) {
-        // lanes without a protected token read the first protected lane's row
-        const int src = (int)__builtin_ctzll(pm);
-        const int pp = prot ? p : __builtin_amdgcn_readlane(p, src);
-        const uint16_t* rowp = pp < n_s ? a.sink + ((int64_t)b * n_sink + pp) * D_ALL
-                                        : a.local + ((int64_t)b * n_local + pp % n_local) * D_ALL;
-        S += bf16_scores(rowp, prot, qA, tile, row, j);
-      }
+    if constexpr (CB == 16) {
+      // BF16 baseline: no protected buffers; a partial last page masks its tail
+      float4v S = bf16_page_scores(t, !mixed || valid, qA, tile, row, j);
       if (!valid) S = (float4v){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      return S;
+    } else {
+      if (mixed) mask_token<CB>(t, valid && !prot);
+      float4v S = packed_scores<CB>(t, qA, qz1, qz2, tile, row, j);
+      if (mixed) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);  // pages with BF16 rows are the slow ones
+        const uint64_t pm = __builtin_amdgcn_ballot_w64(prot);
+        if (pm != 0) {
+          // lanes without a protected token read the first protected lane's row
+          const int src = (int)__builtin_ctzll(pm);
+          const int pp = prot ? p : __builtin_amdgcn_readlane(p, src);
+          const uint16_t* rowp = pp < n_s ? a.sink + ((int64_t)b * n_sink + pp) * D_ALL
+                                          : a.local + ((int64_t)b * n_local + pp % n_local) * D_ALL;
+          S += bf16_scores(rowp, prot, qA, tile, row, j);
+        }
+        if (!valid) S = (float4v){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+      return S;
     }
-    return S;
   };
 
   // Per item: scores, tile rows and softmax of the item, then (after a
@@ -805,7 +879,9 @@ hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
   const int n_u = a.B * a.n_split;
   const dim3 grid((n_u + 7) / 8 * 8 * (a.H / 16));
-  if (c_bits == 4)
+  if (c_bits == 16)
+    decode_kernel<16><<<grid, dim3(256), 0, stream>>>(a);
+  else if (c_bits == 4)
     decode_kernel<4><<<grid, dim3(256), 0, stream>>>(a);
   else
     decode_kernel<2><<<grid, dim3(256), 0, stream>>>(a);

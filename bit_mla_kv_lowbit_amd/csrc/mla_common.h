@@ -7,6 +7,7 @@
 namespace mla {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -35,6 +36,13 @@ struct PageGeom {
   static constexpr int OFF_RS = PAGE * (CC + RC + CS);
   static constexpr int BYTES = PAGE * (CC + RC + CS + RS);
 };
+// BF16 baseline page (CB = 16): 64 rows of [c (512) | k_rope (64)] bf16.
+template <>
+struct PageGeom<16> {
+  static constexpr int ROW = D_ALL * 2;  // bytes per token row (1152)
+  static constexpr int BYTES = PAGE * ROW;
+};
+static_assert(PageGeom<16>::BYTES == 73728, "BF16 page");
 static_assert(PageGeom<4>::BYTES == 23040, "C4R4 page");
 static_assert(PageGeom<2>::BYTES == 14848, "C2R4 page");
 static_assert(PageGeom<4>::OFF_RC == 16384 && PageGeom<4>::OFF_CS == 18432 &&

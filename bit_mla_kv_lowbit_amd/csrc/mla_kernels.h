@@ -20,6 +20,14 @@ struct WriteArgs {
   int n_sink, n_local;
 };
 
+struct QdqArgs {
+  int n_tokens;
+  const uint16_t* c_kv;    // bf16 [n, 512]
+  const uint16_t* k_rope;  // bf16 [n, 64]
+  uint16_t* out_c;         // bf16 [n, 512]
+  uint16_t* out_r;         // bf16 [n, 64]
+};
+
 struct DecodeArgs {
   const uint16_t* q_lat;   // bf16 [B, H, 512]
   const uint16_t* q_rope;  // bf16 [B, H, 64]
@@ -50,7 +58,8 @@ struct SplitPlan {
 SplitPlan plan_splits(int B, int H, int max_pages);
 size_t decode_workspace_bytes(int B, int H, int max_pages);
 
-hipError_t launch_write(const WriteArgs& a, int c_bits, hipStream_t stream);
-hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream);
+hipError_t launch_write(const WriteArgs& a, int c_bits, hipStream_t stream);  // c_bits 16: BF16 pages
+hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream);  // c_bits 16: BF16 pages
+hipError_t launch_qdq(const QdqArgs& a, int c_bits, hipStream_t stream);
 
 }  // namespace mla

@@ -12,6 +12,48 @@
 
 namespace mla {
 
+// Load the 32 bf16 values of one group (64 bytes) and widen them to fp32.
+__device__ __forceinline__ void load_group(const uint16_t* src, u32x4 (&raw)[4],
+                                           float (&x)[GROUP]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) raw[k] = reinterpret_cast<const u32x4*>(src)[k];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * k + 2 * e] = bf16_to_f32(raw[k][e] & 0xffffu);
+      x[8 * k + 2 * e + 1] = bf16_to_f32(raw[k][e] >> 16);
+    }
+  }
+}
+
+// Asymmetric min-max quantization of one group to `bits`-bit codes: fp16
+// scale s = (hi - lo) / (2^bits - 1) and zero z = lo (both rounded to nearest
+// even), q = clamp(rint((x - z) / s), 0, 2^bits - 1), all codes 0 when s = 0.
+__device__ __forceinline__ void quantize_group(const float (&x)[GROUP], int bits, _Float16& s16,
+                                               _Float16& z16, uint32_t (&q)[GROUP]) {
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int i = 1; i < GROUP; ++i) {  // strict compares: the first of equal values wins
+    lo = x[i] < lo ? x[i] : lo;
+    hi = x[i] > hi ? x[i] : hi;
+  }
+  const float qmax = (float)((1 << bits) - 1);
+  const float s32 = __fdiv_rn(__fsub_rn(hi, lo), qmax);
+  s16 = (_Float16)s32;  // round to nearest even
+  z16 = (_Float16)lo;
+  const float s = (float)s16, z = (float)z16;
+#pragma unroll
+  for (int i = 0; i < GROUP; ++i) {
+    float r = 0.0f;
+    if (s != 0.0f) {
+      r = rintf(__fdiv_rn(__fsub_rn(x[i], z), s));
+      r = fminf(fmaxf(r, 0.0f), qmax);
+    }
+    q[i] = (uint32_t)r;
+  }
+}
+
 template <int CB>
 __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
   using G = PageGeom<CB>;
@@ -38,39 +80,11 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
 
   // 32 bf16 values as 16 dwords (64 B)
   u32x4 raw[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) raw[k] = reinterpret_cast<const u32x4*>(src)[k];
   float x[GROUP];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[8 * k + 2 * e] = bf16_to_f32(raw[k][e] & 0xffffu);
-      x[8 * k + 2 * e + 1] = bf16_to_f32(raw[k][e] >> 16);
-    }
-  }
-  float lo = x[0], hi = x[0];
-#pragma unroll
-  for (int i = 1; i < GROUP; ++i) {  // strict compares: the first of equal values wins
-    lo = x[i] < lo ? x[i] : lo;
-    hi = x[i] > hi ? x[i] : hi;
-  }
-  const float qmax = (float)((1 << bits) - 1);
-  const float s32 = __fdiv_rn(__fsub_rn(hi, lo), qmax);
-  const _Float16 s16 = (_Float16)s32;  // round to nearest even
-  const _Float16 z16 = (_Float16)lo;
-  const float s = (float)s16, z = (float)z16;
-
+  load_group(src, raw, x);
+  _Float16 s16, z16;
   uint32_t q[GROUP];
-#pragma unroll
-  for (int i = 0; i < GROUP; ++i) {
-    float r = 0.0f;
-    if (s != 0.0f) {
-      r = rintf(__fdiv_rn(__fsub_rn(x[i], z), s));
-      r = fminf(fmaxf(r, 0.0f), qmax);
-    }
-    q[i] = (uint32_t)r;
-  }
+  quantize_group(x, bits, s16, z16, q);
 
   // pack (code order of the page layout): sub-block j (channels 8j..8j+7 of the
   // group) goes to chunk j of the group's chunk row; channel 8j + 2i + k sits at
@@ -135,8 +149,34 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
   }
 }
 
+// Paired BF16 cache (the unquantized baseline of the Figure 5(b) and Table 9
+// latency comparison): the token's [c | k_rope] row is copied into its page
+// slot. One thread per 16-byte chunk (72 per token), so a wavefront stores
+// whole rows with coalesced 128-bit writes.
+__global__ __launch_bounds__(256) void write_bf16_kernel(WriteArgs a) {
+  constexpr int CH = D_ALL / 8;  // 16-byte chunks per row
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)a.n_tokens * CH) return;
+  const int t = (int)(gid / CH), k = (int)(gid % CH);
+  const int b = a.seq_idx ? a.seq_idx[t] : t;
+  const int p = a.pos[t];
+  if (b < 0 || b >= a.B || p < 0 || p >= a.max_pages * PAGE) return;
+  const int64_t page = a.page_table[(int64_t)b * a.max_pages + p / PAGE];
+  const u32x4 v = k < D_C / 8
+                      ? reinterpret_cast<const u32x4*>(a.c_kv + (int64_t)t * D_C)[k]
+                      : reinterpret_cast<const u32x4*>(a.k_rope + (int64_t)t * D_R)[k - D_C / 8];
+  u32x4* row = reinterpret_cast<u32x4*>(a.pages + page * (int64_t)PageGeom<16>::BYTES +
+                                        (int64_t)(p % PAGE) * PageGeom<16>::ROW);
+  row[k] = v;
+}
+
 hipError_t launch_write(const WriteArgs& a, int c_bits, hipStream_t stream) {
   if (a.n_tokens == 0) return hipSuccess;
+  if (c_bits == 16) {
+    const int64_t total = (int64_t)a.n_tokens * (D_ALL / 8);
+    write_bf16_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(a);
+    return hipGetLastError();
+  }
   const int64_t total = (int64_t)a.n_tokens * (NG_C + NG_R);
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
@@ -144,6 +184,50 @@ hipError_t launch_write(const WriteArgs& a, int c_bits, hipStream_t stream) {
     write_kernel<4><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(a);
   else
     write_kernel<2><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// Simulated quantize-dequantize (Figure 3 caption): one thread per (token,
+// group) quantizes its group as the writer does and stores x^ = q * s + z,
+// one fused multiply-add rounded to fp32, then rounded to bf16 (nearest even).
+template <int CB>
+__global__ __launch_bounds__(256) void qdq_kernel(QdqArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)a.n_tokens * (NG_C + NG_R)) return;
+  const int t = (int)(gid / (NG_C + NG_R));
+  const int g = (int)(gid % (NG_C + NG_R));
+  const bool rope = g >= NG_C;
+  const int gi = rope ? g - NG_C : g;
+  const int64_t off = rope ? (int64_t)t * D_R + gi * GROUP : (int64_t)t * D_C + gi * GROUP;
+  u32x4 raw[4];
+  float x[GROUP];
+  load_group((rope ? a.k_rope : a.c_kv) + off, raw, x);
+  _Float16 s16, z16;
+  uint32_t q[GROUP];
+  quantize_group(x, rope ? 4 : CB, s16, z16, q);
+  const float s = (float)s16, z = (float)z16;
+  u32x4* dst = reinterpret_cast<u32x4*>((rope ? a.out_r : a.out_c) + off);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = __builtin_fmaf((float)q[8 * k + 2 * e], s, z);
+      const float hi = __builtin_fmaf((float)q[8 * k + 2 * e + 1], s, z);
+      v[e] = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    }
+    dst[k] = v;
+  }
+}
+
+hipError_t launch_qdq(const QdqArgs& a, int c_bits, hipStream_t stream) {
+  if (a.n_tokens == 0) return hipSuccess;
+  const int64_t total = (int64_t)a.n_tokens * (NG_C + NG_R);
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (c_bits == 4)
+    qdq_kernel<4><<<grid, dim3(256), 0, stream>>>(a);
+  else
+    qdq_kernel<2><<<grid, dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -165,6 +165,46 @@ int mla_lowbit_write_decode(const mla_lowbit_config* cfg, int B, int H, float so
                             void* sink, void* local, void* out, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/*
+ * Simulated quantize-dequantize, QDQ (Figure 3 caption: the quantizer applied
+ * and undone in place, as calibration and accuracy studies use it). Every
+ * group of every row goes through the writer's quantizer above at cfg's bit
+ * widths and comes back as x^ = q * s + z, rounded once to fp32 (a fused
+ * multiply-add) and then to bf16 (nearest even). Bit-exact; no protection
+ * policy applies (n_sink / n_local are ignored).
+ *   c_kv, k_rope   bf16 [n_tokens, d_c], [n_tokens, d_r]  inputs
+ *   out_c, out_r   bf16 [n_tokens, d_c], [n_tokens, d_r]  outputs (may alias the inputs)
+ */
+int mla_lowbit_qdq(const mla_lowbit_config* cfg, int n_tokens, const void* c_kv,
+                   const void* k_rope, void* out_c, void* out_r, void* stream);
+
+/*
+ * Paired BF16 cache: the unquantized baseline that the low-bit decode is
+ * measured against (Figure 5(b) caption: attention latency normalized to
+ * paired measurements with a BF16 cache; Table 9 caption: delta =
+ * t_C4R4 / t_BF16 - 1). Same paging as the packed cache (64-token pages,
+ * page_table[b][pos / 64], slot pos % 64), d_c = 512, d_r = 64; a page holds
+ * 64 rows of [c_kv (512) | k_rope (64)] bf16 (73728 bytes); no sink or local
+ * buffers. The decode runs the same kernel skeleton as mla_lowbit_decode
+ * (page ranges, one softmax, log-sum-exp merge) with bf16 MFMA on the rows.
+ */
+size_t mla_bf16_page_bytes(void);
+size_t mla_bf16_decode_workspace_bytes(int B, int H, int max_pages);
+
+/* Copy each token's row into its page slot; arguments as in mla_lowbit_write
+ * (tokens outside [0, B) x [0, max_pages * 64) are dropped). */
+int mla_bf16_write(int n_tokens, const void* c_kv, const void* k_rope, const int32_t* seq_idx,
+                   const int32_t* pos, const int32_t* page_table, int B, int max_pages,
+                   void* pages, void* stream);
+
+/* Attention over tokens p < seq_lens[b] of the BF16 cache; arguments and
+ * outputs as in mla_lowbit_decode (workspace of at least
+ * mla_bf16_decode_workspace_bytes(B, H, max_pages) bytes). */
+int mla_bf16_decode(int B, int H, float softmax_scale, const void* q_lat, const void* q_rope,
+                    const void* pages, const int32_t* page_table, int max_pages,
+                    const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

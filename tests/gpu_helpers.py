@@ -55,7 +55,8 @@ def compare_decode(out, lse, ref, ref_lse, rows=None):
         gl = gl.reshape(-1)
     both_empty = np.isneginf(ref_lse) & np.isneginf(gl)
     assert np.array_equal(np.isneginf(ref_lse), np.isneginf(gl)), "empty rows differ"
-    dl = np.abs(np.where(both_empty, 0.0, gl - ref_lse))
+    with np.errstate(invalid="ignore"):  # -inf - -inf on empty rows, masked out
+        dl = np.abs(np.where(both_empty, 0.0, gl - ref_lse))
     nref = np.linalg.norm(ref)
     rel = np.linalg.norm(got - ref) / nref if nref > 0 else np.linalg.norm(got)
     mx = np.max(np.abs(got - ref) / np.maximum(1.0, np.abs(ref))) if ref.size else 0.0

@@ -17,14 +17,16 @@ HEADER = os.path.join(ROOT, "include", "mla_lowbit.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_lowbit_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mla_(?:lowbit|bf16)_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["mla_lowbit_write", "mla_lowbit_decode", "mla_lowbit_write_decode",
               "mla_lowbit_page_bytes", "mla_lowbit_decode_workspace_bytes",
-              "mla_lowbit_strerror", "mla_lowbit_version", "mla_lowbit_check_config"]:
+              "mla_lowbit_strerror", "mla_lowbit_version", "mla_lowbit_check_config",
+              "mla_lowbit_qdq", "mla_bf16_page_bytes", "mla_bf16_decode_workspace_bytes",
+              "mla_bf16_write", "mla_bf16_decode"]:
         assert n in names
 
 
@@ -108,3 +110,52 @@ def test_binding_refuses_cpu_tensors():
     t = torch.zeros(4, 512, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         binding._ptr(t)
+
+
+def test_bf16_size_queries():
+    assert mla.bf16_page_bytes() == 64 * 576 * 2
+    assert mla.bf16_decode_workspace_bytes(8, 16, 512) == mla.decode_workspace_bytes(
+        mla.C4R4, 8, 16, 512)
+    assert mla.bf16_decode_workspace_bytes(8, 24, 512) == 0
+    assert mla.bf16_decode_workspace_bytes(8, 16, 0) == 0
+
+
+def test_bf16_validation_errors():
+    L = mla.lib()
+
+    def dec(B=2, H=16, scale=0.1, ws_bytes=1 << 40, q_lat=_fake(), out=_fake()):
+        return L.mla_bf16_decode(B, H, scale, q_lat, _fake(), _fake(), _fake(), 4, _fake(), out,
+                                 _fake(), _fake(), ws_bytes, None)
+
+    assert dec(H=24) == binding.EINVAL
+    assert dec(B=-1) == binding.EINVAL
+    assert dec(scale=-1.0) == binding.EINVAL
+    assert dec(q_lat=None) == binding.EINVAL
+    assert dec(out=_fake(0x10002)) == binding.EINVAL
+    assert dec(ws_bytes=8) == binding.EWORKSPACE
+    assert dec(B=0) == binding.OK
+
+    def wr(n=4, B=2, max_pages=4, pages=_fake(), seq_idx=_fake()):
+        return L.mla_bf16_write(n, _fake(), _fake(), seq_idx, _fake(), _fake(), B, max_pages,
+                                pages, None)
+
+    assert wr(n=-1) == binding.EINVAL
+    assert wr(pages=None) == binding.EINVAL
+    assert wr(seq_idx=None) == binding.EINVAL
+    assert wr(max_pages=0) == binding.EINVAL
+    assert wr(B=0) == binding.EINVAL
+    assert wr(n=0) == binding.OK
+
+
+def test_qdq_validation_errors():
+    L = mla.lib()
+
+    def call(cfg=mla.C4R4, n=4, out_c=_fake()):
+        c = cfg.c()
+        return L.mla_lowbit_qdq(ctypes.byref(c), n, _fake(), _fake(), out_c, _fake(), None)
+
+    assert call(n=-1) == binding.EINVAL
+    assert call(out_c=None) == binding.EINVAL
+    assert call(out_c=_fake(0x10004)) == binding.EINVAL
+    assert call(cfg=mla.Config(c_bits=8)) == binding.EUNSUPPORTED
+    assert call(n=0) == binding.OK
