@@ -89,6 +89,77 @@ def measured_traffic(workload: str):
         return None
 
 
+def time_steps(launch, R, steps, warmup, eager, outs):
+    """Time `steps` calls of launch(k mod R, stream) after `warmup` untimed ones.
+    Graph mode: the warmup and the timed steps are each captured as one HIP
+    graph; the timed region is one replay bracketed by HIP events on the stream
+    it runs on. Eager mode: every step is launched from Python between its own
+    events. The outputs `outs` of the first eager call must be reproduced by the
+    warmup replay and by the timed steps. Returns (wall ms per step, event ms
+    per step list)."""
+    import torch
+
+    cur = torch.cuda.current_stream()
+    launch(0, cur)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+
+    def same():
+        return all(torch.equal(a, b) for a, b in zip(outs, ref))
+
+    def clear():
+        for t in outs:
+            t.zero_()
+
+    if eager:
+        for k in range(warmup):
+            launch(k % R, cur)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            evs[k][0].record(cur)
+            launch((warmup + k) % R, cur)
+            evs[k][1].record(cur)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ev_ms = [a.elapsed_time(b) for a, b in evs]
+    else:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(cur)
+
+        def capture(first, n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for k in range(first, first + n):
+                    launch(k % R, torch.cuda.current_stream())
+            return g
+
+        g_warm = capture(0, max(1, warmup))
+        g_timed = capture(warmup, steps)
+        cur.wait_stream(cap)
+        torch.cuda.synchronize()
+        clear()
+        g_warm.replay()
+        torch.cuda.synchronize()
+        if not same():
+            raise RuntimeError("warmup graph replay differs from the eager call")
+        clear()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(cur)
+        g_timed.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ev_ms = [e0.elapsed_time(e1) / steps]
+    if not same():
+        raise RuntimeError("timed steps changed the result")
+    return (t1 - t0) * 1e3 / steps, ev_ms
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +170,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying HIP graphs")
+    ap.add_argument("--no-bf16", action="store_true",
+                    help="skip the paired BF16-cache decode of the same batch")
+    ap.add_argument("--sweep", default="",
+                    help="context sweep instead of the workload: comma-separated lengths "
+                         "(e.g. 1024,16384,131072,1048576), C4R4 and BF16 at --sweep-batch")
+    ap.add_argument("--sweep-batch", type=int, default=8)
+    ap.add_argument("--prefill", action="store_true",
+                    help="bulk writer throughput: the workload's whole cache in one write call")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one elementwise copy of this many MiB (fp32 negation), the "
                          "known-size kernel that scales the HBM byte counters")
@@ -125,8 +204,12 @@ def main():
         print(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + "
               f"{args.calib_copy_mib} MiB written", file=sys.stderr, flush=True)
 
+    if args.sweep:
+        return run_sweep(args, [int(x) for x in args.sweep.split(",") if x])
     wl = synth.WORKLOADS[args.workload]
     cfg = mla.Config(c_bits=wl.c_bits)
+    if args.prefill:
+        return run_prefill(args, wl, cfg)
     print(f"[bench] generating {wl.desc} on the GPU", file=sys.stderr, flush=True)
     inp, step = synth.workload_inputs(wl, device=dev)
     lens = (step.seq_lens if step is not None else inp.seq_lens).cpu().tolist()
@@ -158,68 +241,11 @@ def main():
 
     print(f"[bench] cache {cache_bytes / 1e6:.1f} MB x {R} copies; warmup {args.warmup}",
           file=sys.stderr, flush=True)
-    cur = torch.cuda.current_stream()
-    launch(0, cur)
-    torch.cuda.synchronize()
-    eager_out, eager_lse = out.clone(), lse.clone()
-
-    if args.eager:
-        for k in range(args.warmup):
-            launch(k % R, cur)
-        # timed region: exactly K steps, each bracketed by HIP events on the launch stream
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(args.steps):
-            evs[k][0].record(cur)
-            launch((args.warmup + k) % R, cur)
-            evs[k][1].record(cur)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ev_ms = [a.elapsed_time(b) for a, b in evs]
-    else:
-        # the W warmup steps and the K timed steps are each captured in one HIP
-        # graph (step k decodes cache copy k mod R); the timed region is one
-        # replay, bracketed by HIP events on the stream it runs on
-        cap = torch.cuda.Stream()
-        cap.wait_stream(cur)
-
-        def capture(first, n):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                for k in range(first, first + n):
-                    launch(k % R, torch.cuda.current_stream())
-            return g
-
-        g_warm = capture(0, max(1, args.warmup))
-        g_timed = capture(args.warmup, args.steps)
-        cur.wait_stream(cap)
-        torch.cuda.synchronize()
-        out.zero_()
-        lse.zero_()
-        g_warm.replay()
-        torch.cuda.synchronize()
-        if not (torch.equal(out, eager_out) and torch.equal(lse, eager_lse)):
-            raise RuntimeError("warmup graph replay differs from the eager decode")
-        out.zero_()
-        lse.zero_()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record(cur)
-        g_timed.replay()
-        e1.record(cur)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ev_ms = [e0.elapsed_time(e1) / args.steps]
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step, ev_ms = time_steps(launch, R, args.steps, args.warmup, args.eager, (out, lse))
     ev_mean = float(np.mean(ev_ms))
     print(f"[bench] {args.steps} steps ({'eager' if args.eager else 'one graph'}): "
           f"{ms_per_step * 1e3:.1f} us/step wall, {ev_mean * 1e3:.1f} us/step events",
           file=sys.stderr, flush=True)
-    if not (torch.equal(out, eager_out) and torch.equal(lse, eager_lse)):
-        raise RuntimeError("timed steps changed the decode result")
 
     tokens = float(sum(lens))
     value = tokens / (ms_per_step / 1e3)
@@ -249,6 +275,10 @@ def main():
         roof["traffic_fetch_write"] = [tr["fetch_bytes"], tr["write_bytes"]]
         roof["traffic_copy_calibration"] = tr["copy_calibration"]
 
+    paired = None
+    if step is None and not args.no_bf16:
+        paired = paired_bf16(args, wl, inp, ev_mean * 1e3, cache_bytes)
+
     cpu = None
     parity = None
     if not args.no_cpu:
@@ -272,6 +302,7 @@ def main():
                    "tokens_per_step": int(tokens), "cache_copies_rotated": R,
                    "launch": "eager" if args.eager else "one_hip_graph_of_K_steps"},
         "roofline": roof,
+        "paired_bf16": paired,
         "cpu_baseline": cpu,
         "parity": parity,
     }
@@ -350,6 +381,155 @@ def cpu_baseline(cfg, wl, inp, step, out, lse, lens, budget_s):
     parity = {"rows": len(rows), "rel_l2": rel, "max_abs_rel": mx, "lse_abs": dl,
               "pass": bool(rel <= 2e-3 and mx <= 1e-2 and dl <= 1e-3)}
     return cpu, parity
+
+
+def bf16_algorithmic_bytes(lens, H):
+    """Bytes a BF16-cache decode must move: 1152 B per cached token, per (b, h)
+    the query, output and lse, 4 B per page-table entry."""
+    return (sum(L * 1152 + 4 * ((L + 63) // 64) for L in lens)
+            + len(lens) * H * (1152 + 1024 + 4))
+
+
+def _copies(nbytes):
+    """Cache copies to rotate so that consecutive steps miss the Infinity Cache."""
+    return max(1, math.ceil(2 * MALL_BYTES / nbytes) + 1) if nbytes < 2 * MALL_BYTES else 1
+
+
+def time_bf16_decode(args, inp, B, H):
+    """The same batch decoded from a BF16 paged cache (mla_bf16_decode), timed
+    like the low-bit decode. Returns (event us per step, cache bytes)."""
+    import numpy as np
+    import torch
+
+    import bit_mla_kv_lowbit_amd as mla
+    import synth
+
+    dev = inp.q_lat.device
+    pages = mla.allocate_bf16_cache(inp.num_pages, dev)
+    mla.bf16_write(inp.c_kv, inp.k_rope, inp.seq_idx, inp.pos, inp.page_table, pages)
+    torch.cuda.synchronize()
+    nbytes = pages.numel() * 2
+    R = _copies(nbytes)
+    reps = [pages] + [pages.clone() for _ in range(R - 1)]
+    max_pages = inp.page_table.shape[1]
+    ws = torch.empty(max(16, mla.bf16_decode_workspace_bytes(B, H, max_pages)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty(B, H, 512, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+
+    def launch(r, stream):
+        mla.bf16_decode(inp.q_lat, inp.q_rope, reps[r], inp.page_table, inp.seq_lens,
+                        synth.SOFTMAX_SCALE, out=out, lse=lse, workspace=ws, stream=stream)
+
+    _, ev_ms = time_steps(launch, R, args.steps, args.warmup, args.eager, (out, lse))
+    del reps, pages
+    return float(np.mean(ev_ms)) * 1e3, nbytes
+
+
+def paired_bf16(args, wl, inp, t_lowbit_us, lowbit_cache_bytes):
+    """Figure 5(b) / Table 9 of the pages: the low-bit decode's latency against
+    a paired BF16-cache decode of the same batch, delta = t_lowbit / t_bf16 - 1."""
+    lens = inp.seq_lens.cpu().tolist()
+    t_bf16, nbytes = time_bf16_decode(args, inp, wl.B, wl.H)
+    bw = bf16_algorithmic_bytes(lens, wl.H) / (t_bf16 / 1e6) / 1e9
+    print(f"[bench] paired BF16 cache: {t_bf16:.1f} us/step events "
+          f"({bw:.0f} GB/s algorithmic)", file=sys.stderr, flush=True)
+    return {"kernel": "mla_bf16_decode: decode_kernel<BF16 pages> + combine_kernel",
+            "event_us_mean": round(t_bf16, 2), "hbm_frac": round(bw / PEAK_HBM_GBS, 4),
+            "delta_pct": round((t_lowbit_us / t_bf16 - 1.0) * 100.0, 2),
+            "cache_bytes": nbytes, "lowbit_cache_bytes": lowbit_cache_bytes,
+            "cache_compression": round(nbytes / lowbit_cache_bytes, 3)}
+
+
+def run_sweep(args, lengths):
+    """Context sweep (Figure 5 and Table 9 of the pages): for each length, B
+    sequences of H = 16 heads decoded from a C4R4 cache and from a BF16 cache;
+    one JSON line per length with both latencies, delta, throughput and the
+    persistent allocation of both layouts."""
+    import torch
+
+    import bit_mla_kv_lowbit_amd as mla
+    import synth
+
+    dev = torch.device("cuda:0")
+    B, H = args.sweep_batch, 16
+    cfg = mla.C4R4
+    for i, L in enumerate(lengths):
+        print(f"[sweep] B{B} H{H} L{L}: generating", file=sys.stderr, flush=True)
+        inp = synth.bulk_cache_inputs(B, L, H, seed=2000 + i, device=dev)
+        pages, sink, local = mla.allocate_cache(cfg, B, inp.num_pages, dev)
+        mla.write(cfg, inp.c_kv, inp.k_rope, inp.seq_idx, inp.pos, inp.seq_lens,
+                  inp.page_table, pages, sink, local)
+        torch.cuda.synchronize()
+        low_bytes = pages.numel() + 2 * (sink.numel() + local.numel())
+        R = _copies(low_bytes)
+        reps = [(pages, sink, local)] + [(pages.clone(), sink.clone(), local.clone())
+                                         for _ in range(R - 1)]
+        max_pages = inp.page_table.shape[1]
+        ws = torch.empty(max(16, mla.decode_workspace_bytes(cfg, B, H, max_pages)),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty(B, H, 512, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+
+        def launch(r, stream):
+            p, s, l = reps[r]
+            mla.decode(cfg, inp.q_lat, inp.q_rope, p, inp.page_table, inp.seq_lens, s, l,
+                       synth.SOFTMAX_SCALE, out=out, lse=lse, workspace=ws, stream=stream)
+
+        _, ev = time_steps(launch, R, args.steps, args.warmup, args.eager, (out, lse))
+        t_low = sum(ev) / len(ev) * 1e3
+        del reps, pages, sink, local
+        t_bf16, bf16_bytes = time_bf16_decode(args, inp, B, H)
+        lens = [L] * B
+        table_bytes = inp.page_table.numel() * 4
+        line = {"mode": "sweep", "B": B, "H": H, "L": L,
+                "c4r4_us": round(t_low, 2), "bf16_us": round(t_bf16, 2),
+                "delta_pct": round((t_low / t_bf16 - 1.0) * 100.0, 2),
+                "c4r4_tokens_per_s": round(B * L / (t_low / 1e6), 1),
+                "c4r4_hbm_frac": round(algorithmic_bytes(lens, H, 4) / (t_low / 1e6) / 1e9
+                                       / PEAK_HBM_GBS, 4),
+                "bf16_hbm_frac": round(bf16_algorithmic_bytes(lens, H) / (t_bf16 / 1e6) / 1e9
+                                       / PEAK_HBM_GBS, 4),
+                "alloc_c4r4_bytes": low_bytes + table_bytes,
+                "alloc_bf16_bytes": bf16_bytes + table_bytes,
+                "compression": round((bf16_bytes + table_bytes) / (low_bytes + table_bytes), 3)}
+        print(json.dumps(line), flush=True)
+        del inp, ws, out, lse
+        torch.cuda.empty_cache()
+
+
+def run_prefill(args, wl, cfg):
+    """Bulk writer throughput: every token of the workload's cache quantized,
+    packed and (if protected) copied in one mla_lowbit_write call per step."""
+    import numpy as np
+    import torch
+
+    import bit_mla_kv_lowbit_amd as mla
+    import synth
+
+    dev = torch.device("cuda:0")
+    print(f"[prefill] generating {wl.desc} on the GPU", file=sys.stderr, flush=True)
+    inp, _ = synth.workload_inputs(wl, device=dev)
+    pages, sink, local = mla.allocate_cache(cfg, wl.B, inp.num_pages, dev)
+
+    def launch(r, stream):
+        mla.write(cfg, inp.c_kv, inp.k_rope, inp.seq_idx, inp.pos, inp.seq_lens,
+                  inp.page_table, pages, sink, local, stream=stream)
+
+    ms, ev = time_steps(launch, 1, args.steps, args.warmup, args.eager, (pages, sink, local))
+    t = float(np.mean(ev)) * 1e3
+    lens = inp.seq_lens.cpu().tolist()
+    n = int(sum(lens))
+    per_tok = 360 if wl.c_bits == 4 else 232
+    prot = sum(min(L, 4) + max(0, min(128, L - 4)) for L in lens)
+    abytes = n * (1152 + 8 + per_tok) + prot * 1152
+    bw = abytes / (t / 1e6) / 1e9
+    print(json.dumps({"mode": "prefill", "workload": wl.desc, "tokens": n,
+                      "event_us_mean": round(t, 2), "tokens_per_s": round(n / (t / 1e6), 1),
+                      "roofline": {"bound": "hbm", "achieved": round(bw, 1),
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(bw / PEAK_HBM_GBS, 4),
+                                   "algorithmic_bytes_per_launch": abytes}}), flush=True)
 
 
 if __name__ == "__main__":

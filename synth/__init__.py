@@ -222,3 +222,20 @@ def workload_inputs(wl: Workload, device="cpu"):
                       torch.tensor(pre, dtype=torch.int32, device=device),
                       torch.tensor(lens, dtype=torch.int32, device=device))
     return inp, step
+
+
+def bulk_cache_inputs(B: int, L: int, H: int, seed: int, device="cpu", outliers=True):
+    """B sequences of L tokens each, drawn in one shot (same value recipe as
+    build_cache_inputs, not its chunked streams): for large sweeps where the
+    chunk loop would dominate. Tokens are in sequence order."""
+    outl = outlier_channels(seed) if outliers else None
+    n = B * L
+    c_kv = latent_tokens(n, seed, device, outliers=outl)
+    pos = torch.arange(L, dtype=torch.int32, device=device).repeat(B)
+    k_rope = rope_keys(pos, seed + 500_000_000, device)
+    seq_idx = torch.arange(B, dtype=torch.int32, device=device).repeat_interleave(L)
+    pt, total = page_table([L] * B, seed)
+    q_lat, q_rope = queries(B, H, seed + 99, device)
+    return CacheInputs(c_kv=c_kv, k_rope=k_rope, seq_idx=seq_idx, pos=pos,
+                       seq_lens=torch.full((B,), L, dtype=torch.int32, device=device),
+                       page_table=pt.to(device), num_pages=total, q_lat=q_lat, q_rope=q_rope)
