@@ -462,18 +462,25 @@ __device__ __forceinline__ float4v bf16_scores(const uint16_t* rowp, bool use,
   return S;
 }
 
+// Q operands of groups Q_REG .. 17 of the BF16 baseline stay in LDS (one copy
+// per workgroup, read once per page): its next page's raw rows take 72 VGPRs,
+// and with all 18 Q operands in registers as well the kernel would spill.
+constexpr int Q_REG = 10;
+constexpr int Q_LDS = NG_C + NG_R - Q_REG;
+
 // Scores and tile row of a token of a BF16 page (bf16 MFMA on the stored
 // values, fp16 tile); a row with keep false contributes 0 and leaves a zero
-// tile row.
+// tile row. q_lds: the lane's Q operands of groups Q_REG.. (stride 64 lanes).
 __device__ __forceinline__ float4v bf16_page_scores(const PageRegs<16>& t, bool keep,
-                                                    const half8 (&qA)[18], _Float16* tile,
-                                                    int row, int j) {
+                                                    const half8 (&qA)[18], const half8* q_lds,
+                                                    _Float16* tile, int row, int j) {
   float4v S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int g = 0; g < NG_C + NG_R; ++g) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     const u32x4 kv = keep ? t.k[g] : z;
-    S = mma_bf16(qA[g], __builtin_bit_cast(half8, kv), S);
+    const half8 q = g < Q_REG ? qA[g] : q_lds[64 * (g - Q_REG)];
+    S = mma_bf16(q, __builtin_bit_cast(half8, kv), S);
     if (g < NG_C)
       *reinterpret_cast<half8*>(tile + row * TS + GROUP * g + 8 * j) = bf16x8_to_f16x8_rtz(kv);
   }
@@ -534,6 +541,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) int flag[WAVES];
   __shared__ __attribute__((aligned(16))) float lsum[WAVES * 16];
   __shared__ int pids[MAX_ITEMS];  // physical pages of this workgroup's packed items
+  __shared__ __attribute__((aligned(16))) half8 q_lds[CB == 16 ? Q_LDS * 64 : 1];
 
   // All scalar arguments are read up front (one round trip, not one per first
   // use: the length, the page table and the first page already form a chain
@@ -639,7 +647,12 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < NG_C + NG_R; ++g)
       qA[g] = *reinterpret_cast<const half8*>(tile + t16 * QS + group_channel(g, j));
-    if constexpr (CB != 16) {
+    if constexpr (CB == 16) {
+      if (w == 0) {
+#pragma unroll
+        for (int g = Q_REG; g < NG_C + NG_R; ++g) q_lds[64 * (g - Q_REG) + lane] = qA[g];
+      }
+    } else {
     const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
     const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -669,7 +682,6 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   __syncthreads();  // page ids in LDS; Q read out of the tile before it is overwritten
 
   auto score_item = [&](const PageRegs<CB>& cur, int k) {
-    PageRegs<CB> t = cur;
     const int p0 = (it0 + k) * PAGE;
     const bool mixed = p0 < n_s || p0 + PAGE > lo_start;  // not every token packed
     const int p = p0 + row;
@@ -677,10 +689,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     const bool prot = valid && (p < n_s || p >= lo_start);
     if constexpr (CB == 16) {
       // BF16 baseline: no protected buffers; a partial last page masks its tail
-      float4v S = bf16_page_scores(t, !mixed || valid, qA, tile, row, j);
+      float4v S = bf16_page_scores(cur, !mixed || valid, qA, q_lds + lane, tile, row, j);
       if (!valid) S = (float4v){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       return S;
     } else {
+      PageRegs<CB> t = cur;
       if (mixed) mask_token<CB>(t, valid && !prot);
       float4v S = packed_scores<CB>(t, qA, qz1, qz2, tile, row, j);
       if (mixed) {
