@@ -1,10 +1,10 @@
 // Fused cache writer for gfx950 (QuantMLA, Figure 8 caption: a packed copy of
 // every incoming token plus BF16 copies of protected sink and recent tokens).
 //
-// One thread quantizes one 32-channel group of one token (16 content groups +
-// 2 RoPE groups per token), so a token's 18 groups are handled by 18
-// neighbouring lanes and its 1152 input bytes are read in 64-byte pieces.
-// Every fp32 step is a single IEEE operation rounded to nearest even
+// One lane takes 8 channels of a token: a wavefront reads one token's 1 KB
+// content row and writes its packed code row with one instruction each, and
+// the 4 lanes of a 32-channel group exchange their extremes to find the
+// group's scale and zero. Every fp32 step is a single IEEE operation rounded to nearest even
 // (__fsub_rn / __fdiv_rn, no contraction), so the codes and the fp16
 // (scale, zero) pairs are bit-identical to a plain CPU evaluation.
 #include "mla_common.h"
@@ -54,99 +54,198 @@ __device__ __forceinline__ void quantize_group(const float (&x)[GROUP], int bits
   }
 }
 
+// Merge the extremes of this lane with those of quad partner j ^ M (DPP quad
+// permutation), the lower lane's channels counting as earlier.
+template <int M>
+__device__ __forceinline__ void quad_merge(float& lo, float& hi, int j) {
+  constexpr int CTRL = M == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  const float plo = __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, lo), CTRL, 0xF, 0xF, false));
+  const float phi = __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, hi), CTRL, 0xF, 0xF, false));
+  const bool upper = (j & M) != 0;  // this lane holds the later channels
+  const float lo_a = upper ? plo : lo, lo_b = upper ? lo : plo;
+  const float hi_a = upper ? phi : hi, hi_b = upper ? hi : phi;
+  lo = lo_b < lo_a ? lo_b : lo_a;
+  hi = hi_b > hi_a ? hi_b : hi_a;
+}
+
+// Minimum and maximum of a group held by the 4 lanes of a quad (lane j holds
+// channels 8j..8j+7, its own extremes in lo / hi): on equal values (+0 / -0)
+// the earlier channel wins, as in a scan over the group in channel order.
+__device__ __forceinline__ void quad_extremes(float& lo, float& hi, int j) {
+  quad_merge<1>(lo, hi, j);
+  quad_merge<2>(lo, hi, j);
+}
+
+// Quantize and store the 8 channels (sub-block j of group gi) one lane holds
+// of a token's content (rope false) or RoPE part, given the group's lanes in
+// its quad; also its share of the BF16 copy when the token is protected.
 template <int CB>
-__global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
+__device__ __forceinline__ void quantize_store(const WriteArgs& a, const u32x4& raw, bool rope,
+                                               int gi, int j, uint8_t* base, int slot,
+                                               uint16_t* keep) {
   using G = PageGeom<CB>;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)a.n_tokens * (NG_C + NG_R);
-  if (gid >= total) return;
-  const int t = (int)(gid / (NG_C + NG_R));
-  const int g = (int)(gid % (NG_C + NG_R));
-  const int b = a.seq_idx ? a.seq_idx[t] : t;
-  const int p = a.pos[t];
-  // tokens outside the page table (or of no sequence) are dropped, never
-  // written out of bounds
-  if (b < 0 || b >= a.B || p < 0 || p >= a.max_pages * PAGE) return;
-  const int L = a.seq_lens[b];
-  const int64_t page = a.page_table[(int64_t)b * a.max_pages + p / PAGE];
-  const int slot = p % PAGE;
-  uint8_t* base = a.pages + page * (int64_t)G::BYTES;
-
-  const bool rope = g >= NG_C;
-  const int gi = rope ? g - NG_C : g;
   const int bits = rope ? 4 : CB;
-  const uint16_t* src = rope ? a.k_rope + (int64_t)t * D_R + gi * GROUP
-                             : a.c_kv + (int64_t)t * D_C + gi * GROUP;
-
-  // 32 bf16 values as 16 dwords (64 B)
-  u32x4 raw[4];
-  float x[GROUP];
-  load_group(src, raw, x);
-  _Float16 s16, z16;
-  uint32_t q[GROUP];
-  quantize_group(x, bits, s16, z16, q);
-
-  // pack (code order of the page layout): sub-block j (channels 8j..8j+7 of the
-  // group) goes to chunk j of the group's chunk row; channel 8j + 2i + k sits at
-  // bit 16k + bits * (4e + i) of its 32-bit word, e = code block of the group.
-  const uint32_t sz = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
-                      ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
-  if (rope) {
-    // 2 groups per chunk: chunk j = 8 bytes at 8j, word gi
-    uint8_t* row = base + G::OFF_RC + slot * G::RC;
+  float x[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t v = 0;
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = bf16_to_f32(raw[e] & 0xffffu);
+    x[2 * e + 1] = bf16_to_f32(raw[e] >> 16);
+  }
+  float lo = x[0], hi = x[0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        v |= (q[8 * j + 2 * i] << (4 * i)) | (q[8 * j + 2 * i + 1] << (16 + 4 * i));
-      *reinterpret_cast<uint32_t*>(row + 8 * j + 4 * gi) = v;
+  for (int i = 1; i < 8; ++i) {  // strict compares: the first of equal values wins
+    lo = x[i] < lo ? x[i] : lo;
+    hi = x[i] > hi ? x[i] : hi;
+  }
+  quad_extremes(lo, hi, j);
+  const float qmax = (float)((1 << bits) - 1);
+  const _Float16 s16 = (_Float16)__fdiv_rn(__fsub_rn(hi, lo), qmax);  // nearest even
+  const _Float16 z16 = (_Float16)lo;
+  const float s = (float)s16, z = (float)z16;
+  // rint(fl((x - z) / s)) without a correctly rounded division per value:
+  // with rs = rcp(s) (1 ulp), t = d * rs lies within 4e-6 of fl(d / s) while
+  // |d / s| <= 17, so both round to the same integer unless t is within 1e-5
+  // of a half-integer; those values take the exact division. Beyond [-1, 17]
+  // both clamp to the same code.
+  // The exact divisions sit behind a wavefront-uniform branch (rarely taken;
+  // as a per-lane select they would all be executed).
+  // (t is within 1e-5 of a half-integer exactly when |t - rint(t)| > 0.5 - 1e-5;
+  // the subtraction is exact for |t| <= 17.)
+  const float rs = __builtin_amdgcn_rcpf(s);
+  float d[8], r[8];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    d[i] = __fsub_rn(x[i], z);
+    const float t = d[i] * rs;
+    r[i] = rintf(t);
+    near |= __builtin_fabsf(t - r[i]) > 0.5f - 1e-5f;
+  }
+  near = near && s != 0.0f;
+  if (__builtin_amdgcn_ballot_w64(near) != 0) {
+    if (near) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float t = d[i] * rs;
+        if (__builtin_fabsf(t - r[i]) > 0.5f - 1e-5f) r[i] = rintf(__fdiv_rn(d[i], s));
+      }
     }
-  } else if (bits == 4) {
-    // 4 groups per 16-byte chunk: chunk (ld, j) at 16 (4 ld + j), word gi % 4
-    uint8_t* row = base + G::OFF_CC + slot * G::CC;
-    const int ld = gi >> 2, w = gi & 3;
+  }
+  uint32_t q[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t v = 0;
+  for (int i = 0; i < 8; ++i)
+    q[i] = s != 0.0f ? (uint32_t)__builtin_amdgcn_fmed3f(r[i], 0.0f, qmax) : 0u;
+
+  // pack (code order of the page layout): sub-block j of a group goes to chunk
+  // j of the group's chunk row; channel 8j + 2i + k sits at bit 16k + bits *
+  // (4e + i) of its 32-bit word, e = code block of the group.
+  if (rope || bits == 4) {
+    uint32_t v = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        v |= (q[8 * j + 2 * i] << (4 * i)) | (q[8 * j + 2 * i + 1] << (16 + 4 * i));
-      *reinterpret_cast<uint32_t*>(row + 16 * (4 * ld + j) + 4 * w) = v;
-    }
+    for (int i = 0; i < 4; ++i) v |= (q[2 * i] << (4 * i)) | (q[2 * i + 1] << (16 + 4 * i));
+    if (rope)  // 2 groups per 8-byte chunk: chunk j at 8j, word gi
+      *reinterpret_cast<uint32_t*>(base + G::OFF_RC + slot * G::RC + 8 * j + 4 * gi) = v;
+    else  // 4 groups per 16-byte chunk: chunk (ld, j) at 16 (4 ld + j), word gi % 4
+      *reinterpret_cast<uint32_t*>(base + G::OFF_CC + slot * G::CC + 16 * (4 * (gi >> 2) + j) +
+                                   4 * (gi & 3)) = v;
   } else {
     // 8 groups per 16-byte chunk, two per word (code block e): the group owns
     // byte e (even channels) and byte 2 + e (odd channels) of the word
-    uint8_t* row = base + G::OFF_CC + slot * G::CC;
-    const int ld = gi >> 3, w = (gi >> 1) & 3, e = gi & 1;
+    uint32_t vlo = 0, vhi = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo |= q[8 * j + 2 * i] << (2 * i);
-        hi |= q[8 * j + 2 * i + 1] << (2 * i);
-      }
-      uint8_t* wp = row + 16 * (4 * ld + j) + 4 * w;
-      wp[e] = (uint8_t)lo;
-      wp[2 + e] = (uint8_t)hi;
+    for (int i = 0; i < 4; ++i) {
+      vlo |= q[2 * i] << (2 * i);
+      vhi |= q[2 * i + 1] << (2 * i);
     }
+    uint8_t* wp = base + G::OFF_CC + slot * G::CC + 16 * (4 * (gi >> 3) + j) + 4 * ((gi >> 1) & 3);
+    const int e = gi & 1;
+    wp[e] = (uint8_t)vlo;
+    wp[2 + e] = (uint8_t)vhi;
   }
-  uint8_t* szdst = rope ? base + G::OFF_RS + slot * G::RS + gi * 4
-                        : base + G::OFF_CS + slot * G::CS + gi * 4;
-  *reinterpret_cast<uint32_t*>(szdst) = sz;
+  if (j == 0) {
+    const uint32_t sz = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
+    uint8_t* szdst = rope ? base + G::OFF_RS + slot * G::RS + gi * 4
+                          : base + G::OFF_CS + slot * G::CS + gi * 4;
+    *reinterpret_cast<uint32_t*>(szdst) = sz;
+  }
+  if (keep) *reinterpret_cast<u32x4*>(keep + (rope ? D_C : 0) + gi * GROUP + 8 * j) = raw;
+}
 
-  // BF16 retention of protected tokens
-  uint16_t* keep = nullptr;
+// Where token t goes: its page base and slot and its BF16 row (null unless
+// protected); false for a token outside the page table (or of no sequence),
+// which is dropped, never written out of bounds.
+template <int CB>
+__device__ __forceinline__ bool token_dest(const WriteArgs& a, int t, uint8_t*& base, int& slot,
+                                           uint16_t*& keep) {
+  const int b = a.seq_idx ? a.seq_idx[t] : t;
+  const int p = a.pos[t];
+  if (b < 0 || b >= a.B || p < 0 || p >= a.max_pages * PAGE) return false;
+  const int L = a.seq_lens[b];
+  const int64_t page = a.page_table[(int64_t)b * a.max_pages + p / PAGE];
+  base = a.pages + page * (int64_t)PageGeom<CB>::BYTES;
+  slot = p % PAGE;
+  keep = nullptr;
   if (p < a.n_sink)
     keep = a.sink + ((int64_t)b * a.n_sink + p) * D_ALL;
-  else if (p >= L - a.n_local)
+  else if (a.n_local > 0 && p >= L - a.n_local)
     keep = a.local + ((int64_t)b * a.n_local + p % a.n_local) * D_ALL;
-  if (keep) {
-    u32x4* kd = reinterpret_cast<u32x4*>(keep + (rope ? D_C + gi * GROUP : gi * GROUP));
+  return true;
+}
+
+// One wavefront writes TW tokens. Lane l holds channels 8l..8l+7 (group l / 4,
+// sub-block l % 4) of a token's content, so each content pass reads the
+// token's 1 KB row and writes its packed code row with one instruction each;
+// a last pass takes the RoPE parts of all TW tokens (8 lanes each). The 4
+// lanes of a group exchange their extremes to find its scale and zero. All
+// loads of the wavefront (the tokens' indices with scalar loads, then every
+// input row) are issued before the first token is quantized, so the chain of
+// dependent reads is paid once per TW tokens.
+template <int CB>
+__global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
+  constexpr int TW = 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * (blockDim.x >> 6) +
+                                                        (threadIdx.x >> 6)));
+  const int t0 = wave * TW;
+  if (t0 >= a.n_tokens) return;
+  const int nt = min(TW, a.n_tokens - t0);
+  u32x4 raw[TW + 1];
+  const int tr = t0 + (lane >> 3);  // token of this lane's RoPE part
+  const int chr = 8 * (lane & 7);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) kd[k] = raw[k];
+  for (int k = 0; k < TW; ++k)
+    raw[k] = *reinterpret_cast<const u32x4*>(a.c_kv + (int64_t)(t0 + min(k, nt - 1)) * D_C +
+                                             8 * lane);
+  raw[TW] = *reinterpret_cast<const u32x4*>(a.k_rope + (int64_t)min(tr, a.n_tokens - 1) * D_R +
+                                            chr);
+  uint8_t* base[TW];
+  int slot[TW];
+  uint16_t* keep[TW];
+  bool ok[TW];
+#pragma unroll
+  for (int k = 0; k < TW; ++k)
+    ok[k] = k < nt && token_dest<CB>(a, t0 + k, base[k], slot[k], keep[k]);
+#pragma unroll
+  for (int k = 0; k < TW; ++k)
+    if (ok[k]) quantize_store<CB>(a, raw[k], false, lane >> 2, lane & 3, base[k], slot[k], keep[k]);
+  // RoPE parts: the lanes of token k (8k .. 8k + 7) take its destination
+  uint8_t* rb = nullptr;
+  int rslot = 0;
+  uint16_t* rkeep = nullptr;
+  bool rok = false;
+#pragma unroll
+  for (int k = 0; k < TW; ++k) {
+    if ((lane >> 3) == k) {
+      rok = ok[k];
+      rb = base[k];
+      rslot = slot[k];
+      rkeep = keep[k];
+    }
   }
+  if (rok) quantize_store<CB>(a, raw[TW], true, (lane & 7) >> 2, lane & 3, rb, rslot, rkeep);
 }
 
 // Paired BF16 cache (the unquantized baseline of the Figure 5(b) and Table 9
@@ -177,9 +276,9 @@ hipError_t launch_write(const WriteArgs& a, int c_bits, hipStream_t stream) {
     write_bf16_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(a);
     return hipGetLastError();
   }
-  const int64_t total = (int64_t)a.n_tokens * (NG_C + NG_R);
+  const int64_t waves = ((int64_t)a.n_tokens + 7) / 8;  // 8 tokens per wavefront
   const int threads = 256;
-  const int64_t blocks = (total + threads - 1) / threads;
+  const int64_t blocks = (waves * 64 + threads - 1) / threads;
   if (c_bits == 4)
     write_kernel<4><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(a);
   else

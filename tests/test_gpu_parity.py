@@ -63,6 +63,31 @@ def test_writer_degenerate_groups():
 
 
 @pytest.mark.parametrize("c_bits", [4, 2])
+def test_writer_signed_zero_ties(c_bits):
+    """+0 and -0 tie as a group's minimum (or maximum) in different 8-channel
+    sub-blocks: the earlier channel decides the zero point's sign bit, as in
+    the oracle's scan in channel order."""
+    cfg = _cfg(c_bits)
+    inp = synth.build_cache_inputs([64], 16, seed=6, device="cpu")
+    c = inp.c_kv.float().abs() + 0.5                  # positive groups ...
+    r = -(inp.k_rope.float().abs() + 0.5)             # ... and negative RoPE groups
+    for t in range(64):
+        g = t % 16
+        a_, b_ = (3, 20) if t % 2 else (20, 3)        # earlier channel first or second
+        c[t, 32 * g + a_] = 0.0
+        c[t, 32 * g + b_] = -0.0
+        r[t, 32 * (t % 2) + (5 if t % 4 < 2 else 29)] = -0.0
+        r[t, 32 * (t % 2) + (29 if t % 4 < 2 else 5)] = 0.0
+    inp.c_kv = c.to(torch.bfloat16)
+    inp.k_rope = r.to(torch.bfloat16)
+    print(f"[case] writer signed-zero ties c_bits={c_bits}", flush=True)
+    pages, sink, local = gpu_cache(cfg, inp, 1)
+    torch.cuda.synchronize()
+    op, osink, olocal = oracle_cache(ocfg_of(cfg), inp, 1)
+    assert np.array_equal(pages.cpu().numpy(), op)
+
+
+@pytest.mark.parametrize("c_bits", [4, 2])
 @pytest.mark.parametrize("H", [16, 128])
 def test_decode_edge_lengths(c_bits, H):
     cfg = _cfg(c_bits)
