@@ -65,11 +65,12 @@ def decode_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, prefix: str = "decode"):
     """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary of this workload, or None when it is missing or was taken
-    on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.txt")
+    WRITE_SIZE summary of this workload (prefix "decode": mla_lowbit_decode,
+    "bf16_decode": mla_bf16_decode), or None when it is missing or was taken on
+    other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{prefix}_traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -434,8 +435,10 @@ def paired_bf16(args, wl, inp, t_lowbit_us, lowbit_cache_bytes):
     bw = bf16_algorithmic_bytes(lens, wl.H) / (t_bf16 / 1e6) / 1e9
     print(f"[bench] paired BF16 cache: {t_bf16:.1f} us/step events "
           f"({bw:.0f} GB/s algorithmic)", file=sys.stderr, flush=True)
+    tr = measured_traffic(wl.name, "bf16_decode")
     return {"kernel": "mla_bf16_decode: decode_kernel<BF16 pages> + combine_kernel",
             "event_us_mean": round(t_bf16, 2), "hbm_frac": round(bw / PEAK_HBM_GBS, 4),
+            "traffic": tr["bytes_per_call"] if tr else None,
             "delta_pct": round((t_lowbit_us / t_bf16 - 1.0) * 100.0, 2),
             "cache_bytes": nbytes, "lowbit_cache_bytes": lowbit_cache_bytes,
             "cache_compression": round(nbytes / lowbit_cache_bytes, 3)}
