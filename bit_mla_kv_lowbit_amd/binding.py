@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.mla_lowbit_write_decode.argtypes = [P, i32, i32, ctypes.c_float, P, P, P, P, P, P, P, i32,
                                               P, P, P, P, P, P, sz, P]
         L.mla_lowbit_write_decode.restype = i32
+        L.mla_lowbit_decode_mq.argtypes = [P, i32, i32, i32, ctypes.c_float, P, P, P, P, i32,
+                                           P, P, P, P, P, P, sz, P]
+        L.mla_lowbit_decode_mq.restype = i32
         L.mla_lowbit_qdq.argtypes = [P, i32, P, P, P, P, P]
         L.mla_lowbit_qdq.restype = i32
         L.mla_bf16_page_bytes.argtypes = []
@@ -191,6 +194,34 @@ def decode(cfg: Config, q_lat, q_rope, pages, page_table, seq_lens, sink, local,
                                  _ptr(sink), _ptr(local), _ptr(out), _ptr(lse), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream))
     _check("mla_lowbit_decode", rc)
+    return out, lse
+
+
+def decode_mq(cfg: Config, q_lat, q_rope, pages, page_table, seq_lens, sink, local,
+              scale: float, out=None, lse=None, workspace=None, stream=None):
+    """mla_lowbit_decode_mq: q_lat [B, s_q, H, d_c], q_rope [B, s_q, H, d_r]; query token i
+    attends to tokens p < seq_lens[b] - (s_q - 1 - i). Returns (out [B, s_q, H, d_c] bf16,
+    lse [B, s_q, H] fp32)."""
+    _want(q_lat, torch.bfloat16, "q_lat")
+    _want(q_rope, torch.bfloat16, "q_rope")
+    B, s_q, H, _ = q_lat.shape
+    max_pages = page_table.shape[1]
+    dev = q_lat.device
+    if out is None:
+        out = torch.empty(B, s_q, H, cfg.d_c, dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty(B, s_q, H, dtype=torch.float32, device=dev)
+    if workspace is None:
+        need = decode_workspace_bytes(cfg, B, s_q * H, max_pages)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    c = cfg.c()
+    rc = lib().mla_lowbit_decode_mq(ctypes.byref(c), B, s_q, H, float(scale), _ptr(q_lat),
+                                    _ptr(q_rope), _ptr(pages), _ptr(page_table), max_pages,
+                                    _ptr(seq_lens), _ptr(sink), _ptr(local), _ptr(out),
+                                    _ptr(lse), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream(stream))
+    _check("mla_lowbit_decode_mq", rc)
     return out, lse
 
 

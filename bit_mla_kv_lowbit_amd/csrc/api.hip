@@ -87,6 +87,8 @@ DecodeArgs make_decode_args(const mla_lowbit_config* cfg, int B, int H, float so
   a.pages_per_split = sp.pages_per_split;
   a.n_sink = cfg->n_sink;
   a.n_local = cfg->n_local;
+  a.s_q = 1;
+  a.h_per_q = H;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   return a;
 }
@@ -159,6 +161,25 @@ int mla_lowbit_decode(const mla_lowbit_config* cfg, int B, int H, float softmax_
   if (rc || B == 0) return rc;
   DecodeArgs a = make_decode_args(cfg, B, H, softmax_scale, q_lat, q_rope, pages, page_table,
                                   max_pages, seq_lens, sink, local, out, lse, workspace);
+  return launch_decode(a, cfg->c_bits, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_LOWBIT_OK
+             : MLA_LOWBIT_ELAUNCH;
+}
+
+int mla_lowbit_decode_mq(const mla_lowbit_config* cfg, int B, int s_q, int H,
+                         float softmax_scale, const void* q_lat, const void* q_rope,
+                         const void* pages, const int32_t* page_table, int max_pages,
+                         const int32_t* seq_lens, const void* sink, const void* local, void* out,
+                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (s_q < 1 || H <= 0 || H % 16 != 0 || (int64_t)s_q * H > (1 << 20)) return MLA_LOWBIT_EINVAL;
+  const int R = s_q * H;  // rows per sequence
+  int rc = decode_checks(cfg, B, R, softmax_scale, q_lat, q_rope, pages, page_table, max_pages,
+                         seq_lens, sink, local, out, lse, workspace, workspace_bytes);
+  if (rc || B == 0) return rc;
+  DecodeArgs a = make_decode_args(cfg, B, R, softmax_scale, q_lat, q_rope, pages, page_table,
+                                  max_pages, seq_lens, sink, local, out, lse, workspace);
+  a.s_q = s_q;
+  a.h_per_q = H;
   return launch_decode(a, cfg->c_bits, static_cast<hipStream_t>(stream)) == hipSuccess
              ? MLA_LOWBIT_OK
              : MLA_LOWBIT_ELAUNCH;

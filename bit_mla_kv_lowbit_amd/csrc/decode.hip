@@ -497,8 +497,9 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
-// Page range [it0, it0 + n_it) of workgroup `split` (of n_split) of a
-// sequence of L tokens. Pages with protected tokens cost about twice a packed
+// Page range [it0, it0 + n_it) of workgroup `split` (of n_split) over the
+// first L tokens of a sequence whose protected tokens are p < n_s and
+// p >= lo_start. Pages with protected tokens cost about twice a packed
 // page (their BF16 rows are read when they are scored), so the boundaries
 // balance the weight c(i) of pages 0 .. i - 1: one per page, plus one for the
 // sink page and for each page from the one holding the window's first token.
@@ -506,10 +507,8 @@ __device__ __forceinline__ float row_sum(float v) {
 struct PageRange {
   int it0, n_it;
 };
-__device__ __forceinline__ PageRange page_range(int L, int n_sink, int n_local, int split,
+__device__ __forceinline__ PageRange page_range(int L, int n_s, int lo_start, int split,
                                                 int n_split) {
-  const int n_s = min(n_sink, L);
-  const int lo_start = max(n_sink, L - n_local);  // first token of the recent window
   const int n_items = (L + PAGE - 1) / PAGE;
   const int wp = min(lo_start / PAGE, n_items);
   const int sink_w = n_s > 0 ? 1 : 0;
@@ -599,22 +598,28 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   }
   const int Lg = max_pages * PAGE;
   const int* ptab_b = page_table + (int64_t)b * max_pages;
-  const PageRange rg = page_range(Lg, n_sink, n_local, split, n_split);
+  const PageRange rg = page_range(Lg, min(n_sink, Lg), max(n_sink, Lg - n_local), split, n_split);
   const int pid0_g = rg.n_it > 0 ? *(const_i32*)(ptab_b + rg.it0) : 0;
   const int pidm_g = tid < rg.n_it ? ptab_b[rg.it0 + tid] : 0;
 
   // lengths are clamped to what the page table can hold
   const int L = min(max(L_raw, 0), Lg);
   const float sl2 = a.scale_log2;
-  const PageRange rr = L == Lg ? rg : page_range(L, n_sink, n_local, split, n_split);
+  // Token p of a page is taken from the packed codes, or from the BF16 buffers
+  // if it is protected (p < n_s: sink; p >= lo_start: the recent window, ring
+  // slot p mod n_local), or is masked if p >= Lq. With s_q query tokens per
+  // sequence (the last s_q tokens of the cache), the heads of query token qi
+  // attend causally to p < Lq = L - (s_q - 1 - qi); the protected set is the
+  // cache's (its length L).
+  const int n_s = min(n_sink, L);
+  const int lo_start = max(n_sink, L - n_local);  // first token of the recent window
+  const int qi = (hb * 16) / a.h_per_q;
+  const int Lq = max(0, L - (a.s_q - 1 - qi));
+  const PageRange rr = Lq == Lg ? rg : page_range(Lq, n_s, lo_start, split, n_split);
   const int it0 = rr.it0;
   const int n_it = rr.n_it;
   const int n_pk = n_it;  // every item is a page of the page table
-  // Token p of a page is taken from the packed codes, or from the BF16 buffers
-  // if it is protected (p < n_s: sink; p >= lo_start: the recent window, ring
-  // slot p mod n_local), or is masked if p >= L.
-  const int n_s = min(n_sink, L);
-  const int lo_start = max(n_sink, L - n_local);  // first token of the recent window
+  const int mix_from = min(lo_start, Lq);  // pages reaching past it have BF16 or masked rows
   int pid0 = pid0_g, pid_mine = pidm_g;
   if (rr.it0 != rg.it0 || rr.n_it != rg.n_it) {
     pid0 = n_pk > 0 ? *(const_i32*)(ptab_b + it0) : 0;
@@ -683,9 +688,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 
   auto score_item = [&](const PageRegs<CB>& cur, int k) {
     const int p0 = (it0 + k) * PAGE;
-    const bool mixed = p0 < n_s || p0 + PAGE > lo_start;  // not every token packed
+    const bool mixed = p0 < n_s || p0 + PAGE > mix_from;  // not every token packed
     const int p = p0 + row;
-    const bool valid = p < L;
+    const bool valid = p < Lq;
     const bool prot = valid && (p < n_s || p >= lo_start);
     if constexpr (CB == 16) {
       // BF16 baseline: no protected buffers; a partial last page masks its tail

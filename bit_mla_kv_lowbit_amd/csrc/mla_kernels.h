@@ -42,6 +42,9 @@ struct DecodeArgs {
   uint16_t* out;  // bf16 [B, H, 512]
   float* lse;     // fp32 [B, H]
   int B, H, n_split, pages_per_split, n_sink, n_local;
+  // query tokens per sequence and heads per query token (H = s_q * h_per_q
+  // rows per sequence; rows of query token i attend to p < len - (s_q - 1 - i))
+  int s_q, h_per_q;
   float scale_log2;  // softmax_scale * log2(e)
 };
 

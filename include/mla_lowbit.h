@@ -153,6 +153,27 @@ int mla_lowbit_decode(const mla_lowbit_config* cfg, int B, int H, float softmax_
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Multi-query decode over the same cache: s_q query tokens per sequence, the
+ * last s_q tokens of the cache (GQLA card on the cards page: multi-token
+ * prediction verifies s_q = 2 tokens per step). Query token i (0 <= i < s_q)
+ * attends causally, to tokens p < seq_lens[b] - (s_q - 1 - i); which tokens
+ * come from the BF16 buffers is decided by seq_lens[b], as in
+ * mla_lowbit_decode. s_q = 1 is mla_lowbit_decode.
+ *   H            heads per query token, a positive multiple of 16
+ *   q_lat        bf16 [B, s_q, H, d_c];  q_rope  bf16 [B, s_q, H, d_r]
+ *   out          bf16 [B, s_q, H, d_c];  lse     fp32 [B, s_q, H]
+ *   workspace    at least mla_lowbit_decode_workspace_bytes(cfg, B, s_q * H,
+ *                max_pages) bytes
+ * A query token with no token to attend to (seq_lens[b] < s_q - i) gives
+ * out = 0, lse = -inf.
+ */
+int mla_lowbit_decode_mq(const mla_lowbit_config* cfg, int B, int s_q, int H,
+                         float softmax_scale, const void* q_lat, const void* q_rope,
+                         const void* pages, const int32_t* page_table, int max_pages,
+                         const int32_t* seq_lens, const void* sink, const void* local, void* out,
+                         float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One serving step (Figure 8 caption): write one new token per sequence
  * (mla_lowbit_write with n_tokens = B, seq_idx = 0..B-1, pos[b] =
  * seq_lens[b] - 1), then decode every sequence including its new token.

@@ -32,3 +32,22 @@ def oracle_decode(cfg, inp, pages, sink, local, scale, sel=None, p_begin=0, p_en
     return oracle.decode(cfg, scale, u16(inp.q_lat), u16(inp.q_rope), pages,
                          inp.page_table.cpu().numpy(), inp.seq_lens.cpu().numpy(), sink, local,
                          sel=sel, p_begin=p_begin, p_end=p_end)
+
+
+def oracle_decode_mq(cfg, inp, pages, sink, local, scale, s_q: int, H: int):
+    """Multi-query decode by the oracle: q_lat / q_rope hold B x (s_q * H) rows
+    (query token i = rows i*H .. i*H + H - 1); query token i of sequence b
+    attends to tokens p < seq_lens[b] - (s_q - 1 - i). Returns (out [B, s_q, H,
+    d_c], lse [B, s_q, H])."""
+    lens = inp.seq_lens.cpu().numpy()
+    B = len(lens)
+    out = np.zeros((B, s_q, H, cfg.d_c))
+    lse = np.zeros((B, s_q, H))
+    for b in range(B):
+        for i in range(s_q):
+            end = max(0, int(lens[b]) - (s_q - 1 - i))
+            sel = [(b, i * H + h) for h in range(H)]
+            o, l = oracle_decode(cfg, inp, pages, sink, local, scale, sel=sel, p_begin=0,
+                                 p_end=end)
+            out[b, i], lse[b, i] = o, l
+    return out, lse

@@ -25,7 +25,7 @@ def test_header_declares_the_entry_points():
     for n in ["mla_lowbit_write", "mla_lowbit_decode", "mla_lowbit_write_decode",
               "mla_lowbit_page_bytes", "mla_lowbit_decode_workspace_bytes",
               "mla_lowbit_strerror", "mla_lowbit_version", "mla_lowbit_check_config",
-              "mla_lowbit_qdq", "mla_bf16_page_bytes", "mla_bf16_decode_workspace_bytes",
+              "mla_lowbit_qdq", "mla_lowbit_decode_mq", "mla_bf16_page_bytes", "mla_bf16_decode_workspace_bytes",
               "mla_bf16_write", "mla_bf16_decode"]:
         assert n in names
 
@@ -159,3 +159,20 @@ def test_qdq_validation_errors():
     assert call(out_c=_fake(0x10004)) == binding.EINVAL
     assert call(cfg=mla.Config(c_bits=8)) == binding.EUNSUPPORTED
     assert call(n=0) == binding.OK
+
+
+def test_decode_mq_validation_errors():
+    L = mla.lib()
+
+    def call(B=2, s_q=2, H=16, ws_bytes=1 << 40, q_lat=_fake()):
+        c = mla.C4R4.c()
+        return L.mla_lowbit_decode_mq(ctypes.byref(c), B, s_q, H, 0.1, q_lat, _fake(), _fake(),
+                                      _fake(), 4, _fake(), _fake(), _fake(), _fake(), _fake(),
+                                      _fake(), ws_bytes, None)
+
+    assert call(s_q=0) == binding.EINVAL
+    assert call(H=8) == binding.EINVAL  # s_q * H = 16, but a head block would span two tokens
+    assert call(H=24) == binding.EINVAL
+    assert call(q_lat=None) == binding.EINVAL
+    assert call(ws_bytes=16) == binding.EWORKSPACE
+    assert call(B=0) == binding.OK

@@ -17,7 +17,7 @@ import bit_mla_kv_lowbit_amd as mla
 import oracle
 import synth
 from tests.gpu_helpers import (DEV, assert_decode_ok, gpu_cache, gpu_decode, ocfg_of, u16)
-from tests.oracle_helpers import oracle_cache, oracle_decode
+from tests.oracle_helpers import oracle_cache, oracle_decode, oracle_decode_mq
 
 pytestmark = pytest.mark.gpu
 
@@ -373,3 +373,42 @@ def test_full_c2r4_sampled():
 
 def test_full_serve_sampled():
     _full_workload("serve", n_seq=4, n_head=4)
+
+
+MQ_LENS = [1, 2, 3, 4, 5, 64, 65, 66, 131, 132, 133, 134, 197, 1000, 0, 5000]
+
+
+@pytest.mark.parametrize("c_bits,s_q,H", [(4, 2, 16), (4, 4, 16), (2, 2, 16), (4, 2, 128)])
+def test_decode_multi_query(c_bits, s_q, H):
+    """s_q query tokens per sequence (multi-token prediction verification):
+    query i attends to p < L - (s_q - 1 - i); lengths shorter than s_q, window
+    edges and ragged pages."""
+    cfg = _cfg(c_bits)
+    inp = synth.build_cache_inputs(MQ_LENS, s_q * H, seed=500 + s_q + H + c_bits, device="cpu")
+    print(f"[case] multi-query c_bits={c_bits} s_q={s_q} H={H}", flush=True)
+    pages, sink, local = gpu_cache(cfg, inp, len(MQ_LENS))
+    g = lambda t: t.to(DEV)  # noqa: E731
+    B = len(MQ_LENS)
+    ql = g(inp.q_lat).view(B, s_q, H, -1)
+    qr = g(inp.q_rope).view(B, s_q, H, -1)
+    out, lse = mla.decode_mq(cfg, ql, qr, pages, g(inp.page_table), g(inp.seq_lens), sink, local,
+                             synth.SOFTMAX_SCALE)
+    torch.cuda.synchronize()
+    oc = ocfg_of(cfg)
+    op, osink, olocal = oracle_cache(oc, inp, B)
+    ref, ref_lse = oracle_decode_mq(oc, inp, op, osink, olocal, synth.SOFTMAX_SCALE, s_q, H)
+    assert_decode_ok(out.reshape(B * s_q * H, -1), lse.reshape(-1), ref.reshape(-1, 512),
+                     ref_lse.reshape(-1), label=f"mq c{c_bits} s_q{s_q} H{H}")
+
+
+def test_decode_multi_query_one_token_is_decode():
+    cfg = _cfg(4)
+    inp = synth.build_cache_inputs([3000, 131, 0], 16, seed=71, device="cpu")
+    pages, sink, local = gpu_cache(cfg, inp, 3)
+    o1, l1 = gpu_decode(cfg, inp, pages, sink, local)
+    g = lambda t: t.to(DEV)  # noqa: E731
+    o2, l2 = mla.decode_mq(cfg, g(inp.q_lat)[:, None], g(inp.q_rope)[:, None], pages,
+                           g(inp.page_table), g(inp.seq_lens), sink, local, synth.SOFTMAX_SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2[:, 0].view(torch.int16))
+    assert torch.equal(l1, l2[:, 0])

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import synth
-from tests.oracle_helpers import oracle_cache, oracle_decode, u16
+from tests.oracle_helpers import oracle_cache, oracle_decode, oracle_decode_mq, u16
 
 SCALE = synth.SOFTMAX_SCALE
 
@@ -287,3 +287,36 @@ def test_window_exit_incremental_matches_bulk():
         for o, n in zip(off, per):
             a = o + slot * n
             assert np.array_equal(snapshots[p][page, a:a + n], pages[page, a:a + n])
+
+
+@pytest.mark.parametrize("s_q", [1, 2, 3])
+def test_multi_query_causal_equals_sdpa(s_q):
+    """s_q query tokens over an all-protected cache (the last s_q tokens are the
+    queries' own): query i attends to the first L - (s_q - 1 - i) tokens, which
+    is SDPA with a bottom-right causal mask."""
+    cfg = oracle.Cfg()
+    H = 2
+    lens = [9, 2, 1]
+    inp = _inputs(lens, s_q * H, seed=61)
+    pages, sink, local = oracle_cache(cfg, inp, len(lens))
+    out, lse = oracle_decode_mq(cfg, inp, pages, sink, local, SCALE, s_q, H)
+    for b, L in enumerate(lens):
+        c, r = _dense_ref(cfg, inp, b, L)
+        ql = inp.q_lat[b].double().reshape(s_q, H, -1)
+        qr = inp.q_rope[b].double().reshape(s_q, H, -1)
+        q = torch.cat([ql, qr], dim=-1).permute(1, 0, 2)[None]          # [1, H, s_q, 576]
+        k = torch.cat([c, r], dim=-1)[None, None].expand(1, H, -1, -1)  # [1, H, L, 576]
+        v = c[None, None].expand(1, H, -1, -1)
+        pos = torch.arange(L)[None, :]
+        lim = (L - (s_q - 1) + torch.arange(s_q))[:, None]             # exclusive limits
+        mask = pos < lim                                                 # [s_q, L]
+        for i in range(s_q):
+            if int(lim[i]) <= 0:
+                assert np.all(out[b, i] == 0) and np.all(np.isneginf(lse[b, i]))
+                continue
+            ro = torch.nn.functional.scaled_dot_product_attention(
+                q[:, :, i:i + 1], k, v, attn_mask=mask[i:i + 1], scale=SCALE)[0, :, 0]
+            s = SCALE * (q[0, :, i] @ k[0, 0].T)
+            rl = torch.logsumexp(s.masked_fill(~mask[i], float("-inf")), dim=-1)
+            np.testing.assert_allclose(out[b, i], ro.numpy(), rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(lse[b, i], rl.numpy(), rtol=1e-12, atol=1e-12)
