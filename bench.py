@@ -177,6 +177,9 @@ def main():
                     help="context sweep instead of the workload: comma-separated lengths "
                          "(e.g. 1024,16384,131072,1048576), C4R4 and BF16 at --sweep-batch")
     ap.add_argument("--sweep-batch", type=int, default=8)
+    ap.add_argument("--sq", type=int, default=1,
+                    help="query tokens per sequence (multi-token prediction verification: "
+                         "mla_lowbit_decode_mq; the BF16 pairing is skipped)")
     ap.add_argument("--prefill", action="store_true",
                     help="bulk writer throughput: the workload's whole cache in one write call")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -229,10 +232,24 @@ def main():
     out = torch.empty(wl.B, wl.H, 512, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(wl.B, wl.H, dtype=torch.float32, device=dev)
     seq_lens_dev = step.seq_lens if step is not None else inp.seq_lens
+    if args.sq > 1:
+        if step is not None:
+            raise SystemExit("--sq applies to the decode workloads, not the serving step")
+        q_lat, q_rope = synth.queries(wl.B, args.sq * wl.H, wl.seed + 99, dev)
+        q_lat = q_lat.view(wl.B, args.sq, wl.H, -1)
+        q_rope = q_rope.view(wl.B, args.sq, wl.H, -1)
+        ws = torch.empty(max(16, mla.decode_workspace_bytes(cfg, wl.B, args.sq * wl.H,
+                                                            max_pages)),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty(wl.B, args.sq, wl.H, 512, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(wl.B, args.sq, wl.H, dtype=torch.float32, device=dev)
 
     def launch(r, stream):
         p, s, l = reps[r]
-        if step is None:
+        if args.sq > 1:
+            mla.decode_mq(cfg, q_lat, q_rope, p, inp.page_table, seq_lens_dev, s, l,
+                          synth.SOFTMAX_SCALE, out=out, lse=lse, workspace=ws, stream=stream)
+        elif step is None:
             mla.decode(cfg, inp.q_lat, inp.q_rope, p, inp.page_table, seq_lens_dev, s, l,
                        synth.SOFTMAX_SCALE, out=out, lse=lse, workspace=ws, stream=stream)
         else:
@@ -250,8 +267,10 @@ def main():
 
     tokens = float(sum(lens))
     value = tokens / (ms_per_step / 1e3)
-    abytes = algorithmic_bytes(lens, wl.H, wl.c_bits)
-    aflops = algorithmic_flops(lens, wl.H)
+    # s_q query tokens: s_q * H query rows (query i sees s_q - 1 - i fewer tokens)
+    abytes = algorithmic_bytes(lens, args.sq * wl.H, wl.c_bits)
+    aflops = sum(algorithmic_flops([max(0, L - (args.sq - 1 - i)) for L in lens], wl.H)
+                 for i in range(args.sq))
     bw = abytes / (ev_mean / 1e3) / 1e9
     tf = aflops / (ev_mean / 1e3) / 1e12
     hbm_bound = aflops / abytes < PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -277,12 +296,12 @@ def main():
         roof["traffic_copy_calibration"] = tr["copy_calibration"]
 
     paired = None
-    if step is None and not args.no_bf16:
+    if step is None and not args.no_bf16 and args.sq == 1:
         paired = paired_bf16(args, wl, inp, ev_mean * 1e3, cache_bytes)
 
     cpu = None
     parity = None
-    if not args.no_cpu:
+    if not args.no_cpu and args.sq == 1:
         cpu, parity = cpu_baseline(cfg, wl, inp, step, out, lse, lens, args.cpu_seconds)
 
     line = {
@@ -298,7 +317,8 @@ def main():
         "vs_baseline": None,
         "dtype": "u4/u2 codes, f16 MFMA, f32 accumulate",
         "data": "synthetic",
-        "config": {"workload": wl.desc, "B": wl.B, "H": wl.H,
+        "config": {"workload": wl.desc + (f", s_q={args.sq}" if args.sq > 1 else ""),
+                   "B": wl.B, "H": wl.H, "s_q": args.sq,
                    "format": "C4R4" if wl.c_bits == 4 else "C2R4",
                    "tokens_per_step": int(tokens), "cache_copies_rotated": R,
                    "launch": "eager" if args.eager else "one_hip_graph_of_K_steps"},
