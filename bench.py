@@ -180,6 +180,8 @@ def main():
     ap.add_argument("--sq", type=int, default=1,
                     help="query tokens per sequence (multi-token prediction verification: "
                          "mla_lowbit_decode_mq; the BF16 pairing is skipped)")
+    ap.add_argument("--qdq", action="store_true",
+                    help="simulated quantize-dequantize throughput over the workload's tokens")
     ap.add_argument("--prefill", action="store_true",
                     help="bulk writer throughput: the workload's whole cache in one write call")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -214,6 +216,8 @@ def main():
     cfg = mla.Config(c_bits=wl.c_bits)
     if args.prefill:
         return run_prefill(args, wl, cfg)
+    if args.qdq:
+        return run_qdq(args, wl, cfg)
     print(f"[bench] generating {wl.desc} on the GPU", file=sys.stderr, flush=True)
     inp, step = synth.workload_inputs(wl, device=dev)
     lens = (step.seq_lens if step is not None else inp.seq_lens).cpu().tolist()
@@ -548,6 +552,36 @@ def run_prefill(args, wl, cfg):
     abytes = n * (1152 + 8 + per_tok) + prot * 1152
     bw = abytes / (t / 1e6) / 1e9
     print(json.dumps({"mode": "prefill", "workload": wl.desc, "tokens": n,
+                      "event_us_mean": round(t, 2), "tokens_per_s": round(n / (t / 1e6), 1),
+                      "roofline": {"bound": "hbm", "achieved": round(bw, 1),
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(bw / PEAK_HBM_GBS, 4),
+                                   "algorithmic_bytes_per_launch": abytes}}), flush=True)
+
+
+def run_qdq(args, wl, cfg):
+    """QDQ throughput (Figure 3 of the pages: simulated quantize-dequantize):
+    every token of the workload's cache through mla_lowbit_qdq in one call."""
+    import numpy as np
+    import torch
+
+    import bit_mla_kv_lowbit_amd as mla
+    import synth
+
+    dev = torch.device("cuda:0")
+    print(f"[qdq] generating {wl.desc} on the GPU", file=sys.stderr, flush=True)
+    inp, _ = synth.workload_inputs(wl, device=dev)
+    out_c, out_r = torch.empty_like(inp.c_kv), torch.empty_like(inp.k_rope)
+
+    def launch(r, stream):
+        mla.qdq(cfg, inp.c_kv, inp.k_rope, out_c=out_c, out_r=out_r, stream=stream)
+
+    _, ev = time_steps(launch, 1, args.steps, args.warmup, args.eager, (out_c, out_r))
+    t = float(np.mean(ev)) * 1e3
+    n = int(inp.c_kv.shape[0])
+    abytes = n * 2 * 1152
+    bw = abytes / (t / 1e6) / 1e9
+    print(json.dumps({"mode": "qdq", "workload": wl.desc, "tokens": n,
                       "event_us_mean": round(t, 2), "tokens_per_s": round(n / (t / 1e6), 1),
                       "roofline": {"bound": "hbm", "achieved": round(bw, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",

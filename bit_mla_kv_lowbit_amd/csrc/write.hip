@@ -12,48 +12,6 @@
 
 namespace mla {
 
-// Load the 32 bf16 values of one group (64 bytes) and widen them to fp32.
-__device__ __forceinline__ void load_group(const uint16_t* src, u32x4 (&raw)[4],
-                                           float (&x)[GROUP]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) raw[k] = reinterpret_cast<const u32x4*>(src)[k];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[8 * k + 2 * e] = bf16_to_f32(raw[k][e] & 0xffffu);
-      x[8 * k + 2 * e + 1] = bf16_to_f32(raw[k][e] >> 16);
-    }
-  }
-}
-
-// Asymmetric min-max quantization of one group to `bits`-bit codes: fp16
-// scale s = (hi - lo) / (2^bits - 1) and zero z = lo (both rounded to nearest
-// even), q = clamp(rint((x - z) / s), 0, 2^bits - 1), all codes 0 when s = 0.
-__device__ __forceinline__ void quantize_group(const float (&x)[GROUP], int bits, _Float16& s16,
-                                               _Float16& z16, uint32_t (&q)[GROUP]) {
-  float lo = x[0], hi = x[0];
-#pragma unroll
-  for (int i = 1; i < GROUP; ++i) {  // strict compares: the first of equal values wins
-    lo = x[i] < lo ? x[i] : lo;
-    hi = x[i] > hi ? x[i] : hi;
-  }
-  const float qmax = (float)((1 << bits) - 1);
-  const float s32 = __fdiv_rn(__fsub_rn(hi, lo), qmax);
-  s16 = (_Float16)s32;  // round to nearest even
-  z16 = (_Float16)lo;
-  const float s = (float)s16, z = (float)z16;
-#pragma unroll
-  for (int i = 0; i < GROUP; ++i) {
-    float r = 0.0f;
-    if (s != 0.0f) {
-      r = rintf(__fdiv_rn(__fsub_rn(x[i], z), s));
-      r = fminf(fmaxf(r, 0.0f), qmax);
-    }
-    q[i] = (uint32_t)r;
-  }
-}
-
 // Merge the extremes of this lane with those of quad partner j ^ M (DPP quad
 // permutation), the lower lane's channels counting as earlier.
 template <int M>
@@ -78,15 +36,13 @@ __device__ __forceinline__ void quad_extremes(float& lo, float& hi, int j) {
   quad_merge<2>(lo, hi, j);
 }
 
-// Quantize and store the 8 channels (sub-block j of group gi) one lane holds
-// of a token's content (rope false) or RoPE part, given the group's lanes in
-// its quad; also its share of the BF16 copy when the token is protected.
-template <int CB>
-__device__ __forceinline__ void quantize_store(const WriteArgs& a, const u32x4& raw, bool rope,
-                                               int gi, int j, uint8_t* base, int slot,
-                                               uint16_t* keep) {
-  using G = PageGeom<CB>;
-  const int bits = rope ? 4 : CB;
+// Asymmetric min-max quantization of one 32-channel group held by the 4
+// lanes of a quad (lane j: channels 8j .. 8j + 7 in raw, bf16): fp16 scale
+// s = (hi - lo) / (2^bits - 1) and zero z = lo (both rounded to nearest even);
+// the lane's codes q = clamp(rint((x - z) / s), 0, 2^bits - 1), all 0 when
+// s = 0. Every fp32 step matches one IEEE operation rounded to nearest even.
+__device__ __forceinline__ void quantize8(const u32x4& raw, int bits, int j, _Float16& s16,
+                                          _Float16& z16, uint32_t (&q)[8]) {
   float x[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -101,8 +57,8 @@ __device__ __forceinline__ void quantize_store(const WriteArgs& a, const u32x4& 
   }
   quad_extremes(lo, hi, j);
   const float qmax = (float)((1 << bits) - 1);
-  const _Float16 s16 = (_Float16)__fdiv_rn(__fsub_rn(hi, lo), qmax);  // nearest even
-  const _Float16 z16 = (_Float16)lo;
+  s16 = (_Float16)__fdiv_rn(__fsub_rn(hi, lo), qmax);  // nearest even
+  z16 = (_Float16)lo;
   const float s = (float)s16, z = (float)z16;
   // rint(fl((x - z) / s)) without a correctly rounded division per value:
   // with rs = rcp(s) (1 ulp), t = d * rs lies within 4e-6 of fl(d / s) while
@@ -133,10 +89,23 @@ __device__ __forceinline__ void quantize_store(const WriteArgs& a, const u32x4& 
       }
     }
   }
-  uint32_t q[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     q[i] = s != 0.0f ? (uint32_t)__builtin_amdgcn_fmed3f(r[i], 0.0f, qmax) : 0u;
+}
+
+// Quantize and store the 8 channels (sub-block j of group gi) one lane holds
+// of a token's content (rope false) or RoPE part, given the group's lanes in
+// its quad; also its share of the BF16 copy when the token is protected.
+template <int CB>
+__device__ __forceinline__ void quantize_store(const WriteArgs& a, const u32x4& raw, bool rope,
+                                               int gi, int j, uint8_t* base, int slot,
+                                               uint16_t* keep) {
+  using G = PageGeom<CB>;
+  const int bits = rope ? 4 : CB;
+  _Float16 s16, z16;
+  uint32_t q[8];
+  quantize8(raw, bits, j, s16, z16, q);
 
   // pack (code order of the page layout): sub-block j of a group goes to chunk
   // j of the group's chunk row; channel 8j + 2i + k sits at bit 16k + bits *
@@ -286,42 +255,37 @@ hipError_t launch_write(const WriteArgs& a, int c_bits, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Simulated quantize-dequantize (Figure 3 caption): one thread per (token,
-// group) quantizes its group as the writer does and stores x^ = q * s + z,
-// one fused multiply-add rounded to fp32, then rounded to bf16 (nearest even).
+// Simulated quantize-dequantize (Figure 3 caption): one lane per 8 channels
+// (72 per token: 64 content, 8 RoPE; quads never straddle a token), the
+// writer's quantizer, then x^ = q * s + z as one fused multiply-add rounded to
+// fp32 and rounded to bf16 (nearest even); 16 B in and out per lane.
 template <int CB>
 __global__ __launch_bounds__(256) void qdq_kernel(QdqArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)a.n_tokens * (NG_C + NG_R)) return;
-  const int t = (int)(gid / (NG_C + NG_R));
-  const int g = (int)(gid % (NG_C + NG_R));
-  const bool rope = g >= NG_C;
-  const int gi = rope ? g - NG_C : g;
-  const int64_t off = rope ? (int64_t)t * D_R + gi * GROUP : (int64_t)t * D_C + gi * GROUP;
-  u32x4 raw[4];
-  float x[GROUP];
-  load_group((rope ? a.k_rope : a.c_kv) + off, raw, x);
+  if (gid >= (int64_t)a.n_tokens * (D_ALL / 8)) return;
+  const int64_t t = gid / (D_ALL / 8);
+  const int w = (int)(gid % (D_ALL / 8));
+  const bool rope = w >= D_C / 8;
+  const int wl = rope ? w - D_C / 8 : w;  // 8-channel block within the part
+  const int64_t off = rope ? t * D_R + 8 * wl : t * D_C + 8 * wl;
+  const u32x4 raw = *reinterpret_cast<const u32x4*>((rope ? a.k_rope : a.c_kv) + off);
   _Float16 s16, z16;
-  uint32_t q[GROUP];
-  quantize_group(x, rope ? 4 : CB, s16, z16, q);
+  uint32_t q[8];
+  quantize8(raw, rope ? 4 : CB, wl & 3, s16, z16, q);
   const float s = (float)s16, z = (float)z16;
-  u32x4* dst = reinterpret_cast<u32x4*>((rope ? a.out_r : a.out_c) + off);
+  u32x4 v;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    u32x4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = __builtin_fmaf((float)q[8 * k + 2 * e], s, z);
-      const float hi = __builtin_fmaf((float)q[8 * k + 2 * e + 1], s, z);
-      v[e] = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
-    }
-    dst[k] = v;
+  for (int e = 0; e < 4; ++e) {
+    const float lo = __builtin_fmaf((float)q[2 * e], s, z);
+    const float hi = __builtin_fmaf((float)q[2 * e + 1], s, z);
+    v[e] = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
   }
+  *reinterpret_cast<u32x4*>((rope ? a.out_r : a.out_c) + off) = v;
 }
 
 hipError_t launch_qdq(const QdqArgs& a, int c_bits, hipStream_t stream) {
   if (a.n_tokens == 0) return hipSuccess;
-  const int64_t total = (int64_t)a.n_tokens * (NG_C + NG_R);
+  const int64_t total = (int64_t)a.n_tokens * (D_ALL / 8);
   const dim3 grid((unsigned)((total + 255) / 256));
   if (c_bits == 4)
     qdq_kernel<4><<<grid, dim3(256), 0, stream>>>(a);
