@@ -129,3 +129,65 @@ def test_qdq_in_place():
     torch.cuda.synchronize()
     assert np.array_equal(u16(c), rc)
     assert np.array_equal(u16(r), rr)
+
+
+def _replay_check(run, outs, label):
+    """Capture run() in a HIP graph; replay it 4 times, with the outputs
+    scribbled over and an eager run() between replays; every replay must give
+    the eager result."""
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        run(torch.cuda.current_stream())
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for k in range(4):
+        for t in outs:
+            t.view(torch.uint8).fill_(0x5A)
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(outs, ref):
+            assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"{label} replay {k}"
+        run()
+        torch.cuda.synchronize()
+
+
+def test_graph_replay_bf16_decode_mq_and_qdq():
+    inp = synth.build_cache_inputs([3000, 70, 1500], 32, seed=88, device="cpu")
+    g = lambda t: t.to(DEV)  # noqa: E731
+    ql, qr, pt, sl = g(inp.q_lat), g(inp.q_rope), g(inp.page_table), g(inp.seq_lens)
+    B, max_pages = 3, pt.shape[1]
+    print("[case] graph replay: bf16 decode, multi-query decode, qdq", flush=True)
+
+    pages16 = _gpu_bf16_cache(inp)
+    ws = torch.empty(max(16, mla.bf16_decode_workspace_bytes(B, 32, max_pages)),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty(B, 32, 512, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, 32, dtype=torch.float32, device=DEV)
+    _replay_check(lambda stream=None: mla.bf16_decode(ql, qr, pages16, pt, sl,
+                                                      synth.SOFTMAX_SCALE, out=out, lse=lse,
+                                                      workspace=ws, stream=stream),
+                  (out, lse), "bf16 decode")
+
+    cfg = mla.C4R4
+    pages, sink, local = mla.allocate_cache(cfg, B, inp.num_pages, DEV)
+    mla.write(cfg, g(inp.c_kv), g(inp.k_rope), g(inp.seq_idx), g(inp.pos), sl, pt, pages, sink,
+              local)
+    ws2 = torch.empty(max(16, mla.decode_workspace_bytes(cfg, B, 32, max_pages)),
+                      dtype=torch.uint8, device=DEV)
+    out2 = torch.empty(B, 2, 16, 512, dtype=torch.bfloat16, device=DEV)
+    lse2 = torch.empty(B, 2, 16, dtype=torch.float32, device=DEV)
+    ql2, qr2 = ql.view(B, 2, 16, -1), qr.view(B, 2, 16, -1)
+    _replay_check(lambda stream=None: mla.decode_mq(cfg, ql2, qr2, pages, pt, sl, sink, local,
+                                                    synth.SOFTMAX_SCALE, out=out2, lse=lse2,
+                                                    workspace=ws2, stream=stream),
+                  (out2, lse2), "multi-query decode")
+
+    c, r = g(inp.c_kv), g(inp.k_rope)
+    oc, orr = torch.empty_like(c), torch.empty_like(r)
+    _replay_check(lambda stream=None: mla.qdq(cfg, c, r, out_c=oc, out_r=orr, stream=stream),
+                  (oc, orr), "qdq")
