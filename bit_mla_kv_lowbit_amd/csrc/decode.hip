@@ -499,10 +499,12 @@ __device__ __forceinline__ float row_sum(float v) {
 
 // Page range [it0, it0 + n_it) of workgroup `split` (of n_split) over the
 // first L tokens of a sequence whose protected tokens are p < n_s and
-// p >= lo_start. Pages with protected tokens cost about twice a packed
-// page (their BF16 rows are read when they are scored), so the boundaries
-// balance the weight c(i) of pages 0 .. i - 1: one per page, plus one for the
-// sink page and for each page from the one holding the window's first token.
+// p >= lo_start. Pages with protected tokens cost more than a packed page
+// (their BF16 rows are read when they are scored), so the boundaries balance
+// the weight c(i) of pages 0 .. i - 1, in half-page units: 2 per page, 1 more
+// for the sink page and 3 more for each page from the one holding the
+// window's first token (1.5 and 2.5 packed pages; measured against 2 and 2 on
+// the V2-Lite- and C2R4-shaped batches, about 1 % faster).
 // Split s starts at the smallest i with c(i) >= s * W / n_split.
 struct PageRange {
   int it0, n_it;
@@ -512,7 +514,7 @@ __device__ __forceinline__ PageRange page_range(int L, int n_s, int lo_start, in
   const int n_items = (L + PAGE - 1) / PAGE;
   const int wp = min(lo_start / PAGE, n_items);
   const int sink_w = n_s > 0 ? 1 : 0;
-  auto weight_before = [&](int i) { return i + sink_w * min(i, 1) + max(0, i - wp); };
+  auto weight_before = [&](int i) { return 2 * i + sink_w * min(i, 1) + 3 * max(0, i - wp); };
   const int64_t W = weight_before(n_items);
   auto first_item = [&](int s) {
     int lo_i = 0, hi_i = n_items;
@@ -872,13 +874,14 @@ __global__ __launch_bounds__(SL * CL) void combine_kernel(DecodeArgs a) {
 
 SplitPlan plan_splits(int B, int H, int max_pages) {
   // two 4-wave workgroups per CU (256 CUs) when the batch is small; enough
-  // workgroups that none takes more than MAX_ITEMS pages: a share of the page
-  // weight (at most max_pages + 6: the sink page and at most 5 pages of a
-  // 256-token window weigh 2) spans at most its weight + 3 pages
+  // workgroups that none takes more than MAX_ITEMS pages: the page weight is
+  // at most 2 max_pages + 16 (the sink page +1, at most 5 pages of a
+  // 256-token window +3 each) and every page weighs at least 2, so a share
+  // spans fewer than (max_pages + 8) / n + 1 pages
   const int n_hb = H / 16;
   const int64_t base = (int64_t)(B > 0 ? B : 1) * n_hb;
   int n = (int)(512 / base);
-  const int need = (max_pages + 6 + (MAX_ITEMS - 3) - 1) / (MAX_ITEMS - 3);
+  const int need = (max_pages + 8 + (MAX_ITEMS - 4) - 1) / (MAX_ITEMS - 4);
   if (n < need) n = need;
   if (n > max_pages) n = max_pages;
   if (n < 1) n = 1;
