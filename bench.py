@@ -177,6 +177,9 @@ def main():
                     help="context sweep instead of the workload: comma-separated lengths "
                          "(e.g. 1024,16384,131072,1048576), C4R4 and BF16 at --sweep-batch")
     ap.add_argument("--sweep-batch", type=int, default=8)
+    ap.add_argument("--runs", type=int, default=1,
+                    help="sweep: independent timing runs per length; with --eager each gives "
+                         "--steps samples (the pages' Table 9 protocol is 2 runs x 60 samples)")
     ap.add_argument("--sq", type=int, default=1,
                     help="query tokens per sequence (multi-token prediction verification: "
                          "mla_lowbit_decode_mq; the BF16 pairing is skipped)")
@@ -299,6 +302,8 @@ def main():
         roof["traffic_fetch_write"] = [tr["fetch_bytes"], tr["write_bytes"]]
         roof["traffic_copy_calibration"] = tr["copy_calibration"]
 
+    roof["copy_GBps"] = copy_bandwidth()
+
     paired = None
     if step is None and not args.no_bf16 and args.sq == 1:
         paired = paired_bf16(args, wl, inp, ev_mean * 1e3, cache_bytes)
@@ -408,6 +413,26 @@ def cpu_baseline(cfg, wl, inp, step, out, lse, lens, budget_s):
     return cpu, parity
 
 
+def copy_bandwidth(nbytes=1 << 30, reps=5):
+    """Achievable read + write bandwidth of a device-to-device copy of nbytes
+    (context for the HBM fraction, not its denominator)."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    return round(2 * nbytes / t / 1e9, 1)
+
+
 def bf16_algorithmic_bytes(lens, H):
     """Bytes a BF16-cache decode must move: 1152 B per cached token, per (b, h)
     the query, output and lse, 4 B per page-table entry."""
@@ -446,8 +471,11 @@ def time_bf16_decode(args, inp, B, H):
         mla.bf16_decode(inp.q_lat, inp.q_rope, reps[r], inp.page_table, inp.seq_lens,
                         synth.SOFTMAX_SCALE, out=out, lse=lse, workspace=ws, stream=stream)
 
-    _, ev_ms = time_steps(launch, R, args.steps, args.warmup, args.eager, (out, lse))
+    ev_ms = []
+    for _ in range(max(1, args.runs)):
+        ev_ms += time_steps(launch, R, args.steps, args.warmup, args.eager, (out, lse))[1]
     del reps, pages
+    time_bf16_decode.samples_us = [v * 1e3 for v in ev_ms]
     return float(np.mean(ev_ms)) * 1e3, nbytes
 
 
@@ -503,8 +531,11 @@ def run_sweep(args, lengths):
             mla.decode(cfg, inp.q_lat, inp.q_rope, p, inp.page_table, inp.seq_lens, s, l,
                        synth.SOFTMAX_SCALE, out=out, lse=lse, workspace=ws, stream=stream)
 
-        _, ev = time_steps(launch, R, args.steps, args.warmup, args.eager, (out, lse))
+        ev = []
+        for _ in range(max(1, args.runs)):
+            ev += time_steps(launch, R, args.steps, args.warmup, args.eager, (out, lse))[1]
         t_low = sum(ev) / len(ev) * 1e3
+        low_samples = [v * 1e3 for v in ev]
         del reps, pages, sink, local
         t_bf16, bf16_bytes = time_bf16_decode(args, inp, B, H)
         lens = [L] * B
@@ -520,6 +551,16 @@ def run_sweep(args, lengths):
                 "alloc_c4r4_bytes": low_bytes + table_bytes,
                 "alloc_bf16_bytes": bf16_bytes + table_bytes,
                 "compression": round((bf16_bytes + table_bytes) / (low_bytes + table_bytes), 3)}
+        if args.eager:
+            import numpy as np
+
+            def stats(v):
+                return {"n": len(v), "mean": round(float(np.mean(v)), 2),
+                        "median": round(float(np.median(v)), 2),
+                        "p10": round(float(np.percentile(v, 10)), 2),
+                        "p90": round(float(np.percentile(v, 90)), 2)}
+            line["c4r4_us_samples"] = stats(low_samples)
+            line["bf16_us_samples"] = stats(time_bf16_decode.samples_us)
         print(json.dumps(line), flush=True)
         del inp, ws, out, lse
         torch.cuda.empty_cache()
