@@ -400,6 +400,19 @@ def cpu_baseline(cfg, wl, inp, step, out, lse, lens, budget_s):
            "sample": f"{len(done)} of {wl.B} sequences ({tok_seq} cache tokens) x all {wl.H} "
                      f"heads, fp64 plain-loop decode, {passes} pass(es), {n_tok} tokens attended "
                      f"in {spent:.1f} s"}
+    if wl.name == "tiny":
+        # the single-core time of the whole tiny workload, next to the all-core one
+        n_thr = oracle.num_threads()
+        oracle.set_num_threads(1)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(budget_s, 5.0):
+            oracle.decode(oc, synth.SOFTMAX_SCALE, ql, qr, op, pt, final, osink, olocal,
+                          sel=[(b, h) for b in done for h in range(wl.H)])
+            reps += 1
+        t1 = time.perf_counter()
+        oracle.set_num_threads(n_thr)
+        cpu["single_core_value"] = round(reps * tok_seq / (t1 - t0), 1)
     rows = [(b, h) for b in done for h in range(wl.H)]
     ref = np.concatenate([refs[b] for b in done])
     rl = np.concatenate([ref_lse[b] for b in done])

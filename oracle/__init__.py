@@ -96,6 +96,8 @@ def lib():
         L.orc_bf16_decode.restype = i32
         L.orc_qdq.argtypes = [P, i32, P, P, P, P]
         L.orc_qdq.restype = i32
+        L.orc_set_num_threads.argtypes = [i32]
+        L.orc_set_num_threads.restype = None
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = i32
         _lib = L
@@ -121,6 +123,10 @@ def _i32(a) -> np.ndarray:
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().orc_set_num_threads(int(n))
 
 
 def f32_to_f16_bits(x: float) -> int:

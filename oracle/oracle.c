@@ -57,6 +57,14 @@ int orc_num_threads(void) {
 #endif
 }
 
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int orc_check_cfg(const orc_cfg* c) {
   if (!c) return -1;
   if (c->c_bits != 2 && c->c_bits != 4) return -1;

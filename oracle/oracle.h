@@ -120,8 +120,9 @@ int orc_bf16_decode(const orc_cfg* cfg, int B, int H, double scale, const uint16
 int orc_qdq(const orc_cfg* cfg, int n_tokens, const uint16_t* c_kv, const uint16_t* k_rope,
             uint16_t* out_c, uint16_t* out_r);
 
-/* Threads the oracle's parallel loops use. */
+/* Threads the oracle's parallel loops use, and a way to change it (n > 0). */
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
