@@ -47,9 +47,15 @@
  *   content (s,z)  [64][16][2] fp16    at 18432 | 10240
  *   RoPE (s,z)     [64][2][2] fp16     at 22528 | 14336
  *   page bytes     23040 | 14848       (360 | 232 B per token)
- * Code order: each little-endian 32-bit word holds 32/b consecutive channels;
- * channel 2a+k of the word (k = 0, 1) sits in code slot a + k * 16/b, i.e.
- * even channels fill the low half-word and odd channels the high half-word.
+ * Code order inside a token's code row (little-endian 32-bit words; channel
+ * c of group g is 32 g + 8 j + 2 i + k with sub-block j, pair i = 0..3, k = 0, 1):
+ *   content, 4-bit: 16-byte chunk (j, l = g div 4) at byte 16 (4 l + j), word
+ *     g mod 4, channel at bit 16 k + 4 i;
+ *   content, 2-bit: 16-byte chunk (j, l = g div 8) at byte 16 (4 l + j), word
+ *     (g mod 8) div 2, channel at bit 16 k + 8 (g mod 2) + 2 i;
+ *   RoPE, 4-bit: 8-byte chunk j at byte 8 j, word g, channel at bit 16 k + 4 i.
+ * So one 16-byte load gives the same 8 channels of 4 (or 8) groups, and even
+ * channels sit in the low half-word, odd ones in the high half-word.
  *
  * Protected tokens (sink / local buffers, bf16 [B][n][d_c + d_r], row =
  * [c_kv | k_rope]): token p of a sequence of length L is read from

@@ -170,3 +170,39 @@ def test_page_sizes_of_the_workload_layouts():
     assert oracle.page_bytes(c2) == 64 * 232 == 14848
     assert oracle.page_regions(c4) == [0, 16384, 18432, 22528]
     assert oracle.page_regions(c2) == [0, 8192, 10240, 14336]
+
+
+@pytest.mark.parametrize("c_bits", [4, 2])
+def test_code_order_as_documented(c_bits):
+    """The content code row follows the order include/mla_lowbit.h states:
+    channel 32 g + 8 j + 2 i + k sits in 16-byte chunk (j, g div (16 / c_bits)),
+    word (g mod 4) for 4-bit or ((g mod 8) div 2) for 2-bit, at bit 16 k + 4 i
+    (4-bit) or 16 k + 8 (g mod 2) + 2 i (2-bit)."""
+    cfg = oracle.Cfg(c_bits=c_bits, n_sink=0, n_local=0)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((1, 512)).astype(np.float32)
+    xr = rng.standard_normal((1, 64)).astype(np.float32)
+
+    def bf16(a):
+        u = a.view(np.uint32)
+        return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+    pages = np.zeros((1, oracle.page_bytes(cfg)), np.uint8)
+    sink = np.zeros((1, 1, 576), np.uint16)
+    local = np.zeros((1, 1, 576), np.uint16)
+    oracle.write(cfg, bf16(x), bf16(xr), np.array([0]), np.array([0]), np.array([1]),
+                 np.array([[0]]), pages, sink, local)
+    off = oracle.page_regions(cfg)
+    words = pages[0, off[0]:off[0] + 512 * c_bits // 8].copy().view("<u4")
+    for g in range(16):
+        xs = (bf16(x)[0, 32 * g:32 * g + 32].astype(np.uint32) << 16).view(np.float32)
+        _, _, q = oracle.quantize_group(xs, c_bits)
+        for j in range(4):
+            for i in range(4):
+                for k in range(2):
+                    if c_bits == 4:
+                        w, bit, m = words[4 * (4 * (g // 4) + j) + g % 4], 16 * k + 4 * i, 15
+                    else:
+                        w, bit, m = (words[4 * (4 * (g // 8) + j) + (g % 8) // 2],
+                                     16 * k + 8 * (g % 2) + 2 * i, 3)
+                    assert (int(w) >> bit) & m == q[8 * j + 2 * i + k]
