@@ -412,3 +412,69 @@ def test_decode_multi_query_one_token_is_decode():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2[:, 0].view(torch.int16))
     assert torch.equal(l1, l2[:, 0])
+
+
+PROT_LENS = [0, 1, 5, 63, 64, 65, 130, 300, 1000, 3000]
+
+
+@pytest.mark.parametrize("c_bits,n_sink,n_local", [(4, 0, 0), (4, 0, 128), (4, 4, 0),
+                                                   (4, 64, 256), (4, 1, 1), (2, 16, 200)])
+def test_protection_settings(c_bits, n_sink, n_local):
+    """Other sink / window sizes the ABI accepts (no sink, no window, a sink that
+    fills a page, a 256-token window over five pages, single tokens): writer
+    bytes, plain and multi-query decode, and one serving step."""
+    cfg = mla.Config(c_bits=c_bits, n_sink=n_sink, n_local=n_local)
+    oc = ocfg_of(cfg)
+    H, B = 16, len(PROT_LENS)
+    inp = synth.build_cache_inputs(PROT_LENS, 2 * H, seed=900 + n_sink + n_local + c_bits,
+                                   device="cpu")
+    print(f"[case] protection c_bits={c_bits} n_sink={n_sink} n_local={n_local}", flush=True)
+    pages, sink, local = gpu_cache(cfg, inp, B, canary=0x3C)
+    torch.cuda.synchronize()
+    op, osink, olocal = oracle_cache(oc, inp, B, canary=0x3C)
+    assert np.array_equal(pages.cpu().numpy(), op)
+    assert np.array_equal(u16(sink), osink)
+    assert np.array_equal(u16(local), olocal)
+    g = lambda t: t.to(DEV)  # noqa: E731
+    # multi-query decode (s_q = 2, H = 16 each), then the plain decode of all 32 rows
+    out, lse = mla.decode_mq(cfg, g(inp.q_lat).view(B, 2, H, -1), g(inp.q_rope).view(B, 2, H, -1),
+                             pages, g(inp.page_table), g(inp.seq_lens), sink, local,
+                             synth.SOFTMAX_SCALE)
+    out1, lse1 = gpu_decode(cfg, inp, pages, sink, local)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_decode_mq(oc, inp, op, osink, olocal, synth.SOFTMAX_SCALE, 2, H)
+    assert_decode_ok(out.reshape(-1, 512), lse.reshape(-1), ref.reshape(-1, 512),
+                     ref_lse.reshape(-1), label=f"prot mq s{n_sink} l{n_local}")
+    r1, rl1 = oracle_decode(oc, inp, op, osink, olocal, synth.SOFTMAX_SCALE)
+    assert_decode_ok(out1, lse1, r1, rl1, label=f"prot s{n_sink} l{n_local}")
+    # one serving step: a new token at position L of every sequence
+    new_lens = [L + 1 for L in PROT_LENS]
+    step_inp = synth.build_cache_inputs(new_lens, 2 * H, seed=901 + n_sink + n_local,
+                                        device="cpu")
+    pt = torch.tensor(np.array(
+        [np.pad(inp.page_table[b].numpy(), (0, 1), constant_values=-1) for b in range(B)]))
+    extra = [b for b, L in enumerate(PROT_LENS) if L % 64 == 0]  # needs a new page
+    num_pages = inp.num_pages
+    for b in extra:
+        pt[b, PROT_LENS[b] // 64] = num_pages
+        num_pages += 1
+    pages2 = torch.full((num_pages, pages.shape[1]), 0x3C, dtype=torch.uint8, device=DEV)
+    pages2[:inp.num_pages] = pages
+    sel = torch.tensor([int(np.flatnonzero(step_inp.seq_idx.numpy() == b)[-1]) if new_lens[b] else 0
+                        for b in range(B)])
+    c_new, r_new = step_inp.c_kv[sel], step_inp.k_rope[sel]
+    pos = torch.tensor(PROT_LENS, dtype=torch.int32)
+    lens_new = torch.tensor(new_lens, dtype=torch.int32)
+    out2, lse2 = mla.write_decode(cfg, g(c_new), g(r_new), g(pos), g(inp.q_lat), g(inp.q_rope),
+                                  pages2, g(pt), g(lens_new), sink, local, synth.SOFTMAX_SCALE)
+    torch.cuda.synchronize()
+    op2 = np.full((num_pages, op.shape[1]), 0x3C, np.uint8)
+    op2[:inp.num_pages] = op
+    oracle.write(oc, u16(c_new), u16(r_new), np.arange(B, dtype=np.int32), pos.numpy(),
+                 lens_new.numpy(), pt.numpy(), op2, osink, olocal)
+    assert np.array_equal(pages2.cpu().numpy(), op2)
+    assert np.array_equal(u16(sink), osink)
+    assert np.array_equal(u16(local), olocal)
+    r2, rl2 = oracle.decode(oc, synth.SOFTMAX_SCALE, u16(inp.q_lat), u16(inp.q_rope), op2,
+                            pt.numpy(), lens_new.numpy(), osink, olocal)
+    assert_decode_ok(out2, lse2, r2, rl2, label=f"prot step s{n_sink} l{n_local}")
