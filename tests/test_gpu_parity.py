@@ -7,7 +7,11 @@ CPU oracle on the same seeded inputs.
   against the fp64 oracle, on edge lengths (all-protected, window edges, ragged
   last pages, empty sequences), both code widths and H in {16, 128}; at the
   full workload sizes on sampled (sequence, head) rows in the same launch
-  configuration the bench times.
+  configuration the bench times;
+* multi-query decode (s_q query tokens per sequence, causal) against the
+  oracle's per-token ranges; s_q = 1 is bit-identical to the plain decode;
+* other sink / window sizes (none, a page-wide sink, a five-page window,
+  single tokens), including a serving step that opens new pages.
 """
 import numpy as np
 import pytest
