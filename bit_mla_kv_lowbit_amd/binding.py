@@ -204,9 +204,17 @@ def decode_mq(cfg: Config, q_lat, q_rope, pages, page_table, seq_lens, sink, loc
     lse [B, s_q, H] fp32)."""
     _want(q_lat, torch.bfloat16, "q_lat")
     _want(q_rope, torch.bfloat16, "q_rope")
+    if q_lat.dim() != 4 or q_lat.shape[3] != cfg.d_c:
+        raise ValueError("q_lat must be [B, s_q, H, d_c]")
     B, s_q, H, _ = q_lat.shape
+    if q_rope.shape != (B, s_q, H, cfg.d_r):
+        raise ValueError("q_rope must be [B, s_q, H, d_r]")
     max_pages = page_table.shape[1]
     dev = q_lat.device
+    if out is not None and out.shape != (B, s_q, H, cfg.d_c):
+        raise ValueError("out must be [B, s_q, H, d_c]")
+    if lse is not None and lse.shape != (B, s_q, H):
+        raise ValueError("lse must be [B, s_q, H]")
     if out is None:
         out = torch.empty(B, s_q, H, cfg.d_c, dtype=torch.bfloat16, device=dev)
     if lse is None:
@@ -261,6 +269,8 @@ def qdq(cfg: Config, c_kv, k_rope, out_c=None, out_r=None, stream=None):
         out_c = torch.empty_like(c_kv)
     if out_r is None:
         out_r = torch.empty_like(k_rope)
+    if out_c.shape != c_kv.shape or out_r.shape != k_rope.shape:
+        raise ValueError("out_c / out_r must match c_kv / k_rope")
     c = cfg.c()
     rc = lib().mla_lowbit_qdq(ctypes.byref(c), n, _ptr(c_kv), _ptr(k_rope), _ptr(out_c),
                               _ptr(out_r), _stream(stream))
@@ -289,8 +299,10 @@ def bf16_write(c_kv, k_rope, seq_idx, pos, page_table, pages, stream=None) -> No
     for n, t in (("seq_idx", seq_idx), ("pos", pos), ("page_table", page_table)):
         _want(t, torch.int32, n)
     n = int(seq_idx.numel())
-    if c_kv.shape[0] != n or k_rope.shape[0] != n or pos.numel() != n:
+    if c_kv.shape != (n, 512) or k_rope.shape != (n, 64) or pos.numel() != n:
         raise ValueError("c_kv / k_rope / pos do not match seq_idx")
+    if pages.dtype != torch.bfloat16 or pages.dim() != 3 or pages.shape[1:] != (64, 576):
+        raise ValueError("pages must be bf16 [num_pages, 64, 576]")
     B, max_pages = page_table.shape
     rc = lib().mla_bf16_write(n, _ptr(c_kv), _ptr(k_rope), _ptr(seq_idx), _ptr(pos),
                               _ptr(page_table), B, max_pages, _ptr(pages), _stream(stream))
@@ -302,7 +314,13 @@ def bf16_decode(q_lat, q_rope, pages, page_table, seq_lens, scale: float, out=No
     """mla_bf16_decode. Returns (out bf16 [B,H,512], lse fp32 [B,H])."""
     _want(q_lat, torch.bfloat16, "q_lat")
     _want(q_rope, torch.bfloat16, "q_rope")
+    if q_lat.dim() != 3 or q_lat.shape[2] != 512:
+        raise ValueError("q_lat must be [B, H, 512]")
     B, H, d_c = q_lat.shape
+    if q_rope.shape != (B, H, 64):
+        raise ValueError("q_rope must be [B, H, 64]")
+    if pages.dtype != torch.bfloat16 or pages.dim() != 3 or pages.shape[1:] != (64, 576):
+        raise ValueError("pages must be bf16 [num_pages, 64, 576]")
     max_pages = page_table.shape[1]
     dev = q_lat.device
     if out is None:
