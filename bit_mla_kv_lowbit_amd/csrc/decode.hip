@@ -35,6 +35,13 @@
 // other's score loop. The partials (O / l, log-sum-exp) of the workgroups of a sequence are merged by
 // combine_kernel (split-K over the sequence with an LSE combine: one global
 // softmax); a sequence with a single page range writes its output directly.
+//
+// The same kernel serves two related calls. With s_q query tokens per
+// sequence (multi-token prediction, GQLA card) the rows of query token i form
+// their own head blocks and attend to the first L - (s_q - 1 - i) tokens. With
+// CB = 16 it decodes the paired BF16 cache the pages normalize their latency
+// to (Figure 5(b), Table 9): BF16 rows instead of codes, bf16 MFMA for the
+// scores, the same tile, softmax, PV and combine.
 #include "mla_common.h"
 #include "mla_kernels.h"
 

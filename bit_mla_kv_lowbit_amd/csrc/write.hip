@@ -4,9 +4,15 @@
 // One lane takes 8 channels of a token: a wavefront reads one token's 1 KB
 // content row and writes its packed code row with one instruction each, and
 // the 4 lanes of a 32-channel group exchange their extremes to find the
-// group's scale and zero. Every fp32 step is a single IEEE operation rounded to nearest even
-// (__fsub_rn / __fdiv_rn, no contraction), so the codes and the fp16
-// (scale, zero) pairs are bit-identical to a plain CPU evaluation.
+// group's scale and zero. The codes and the fp16 (scale, zero) pairs are
+// bit-identical to a plain CPU evaluation with fp32 subtraction and correctly
+// rounded division (nearest even): a reciprocal estimate decides each code
+// whose quotient is not within 1e-5 of a half-integer, the others take the
+// correctly rounded division.
+//
+// Also here: the writer of the paired BF16 cache (rows copied into page
+// slots) and the simulated quantize-dequantize (Figure 3 caption), which
+// shares the quantizer.
 #include "mla_common.h"
 #include "mla_kernels.h"
 
