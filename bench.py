@@ -305,8 +305,8 @@ def main():
     roof["copy_GBps"] = copy_bandwidth()
 
     paired = None
-    if step is None and not args.no_bf16 and args.sq == 1:
-        paired = paired_bf16(args, wl, inp, ev_mean * 1e3, cache_bytes)
+    if not args.no_bf16 and args.sq == 1:
+        paired = paired_bf16(args, wl, inp, ev_mean * 1e3, cache_bytes, step)
 
     cpu = None
     parity = None
@@ -458,9 +458,11 @@ def _copies(nbytes):
     return max(1, math.ceil(2 * MALL_BYTES / nbytes) + 1) if nbytes < 2 * MALL_BYTES else 1
 
 
-def time_bf16_decode(args, inp, B, H):
+def time_bf16_decode(args, inp, B, H, step=None):
     """The same batch decoded from a BF16 paged cache (mla_bf16_decode), timed
-    like the low-bit decode. Returns (event us per step, cache bytes)."""
+    like the low-bit decode; with a serving step, each step first writes the new
+    tokens (mla_bf16_write) and then decodes. Returns (event us per step, cache
+    bytes)."""
     import numpy as np
     import torch
 
@@ -480,8 +482,15 @@ def time_bf16_decode(args, inp, B, H):
     out = torch.empty(B, H, 512, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(B, H, dtype=torch.float32, device=dev)
 
+    lens = inp.seq_lens if step is None else step.seq_lens
+    if step is not None:
+        seq_ids = torch.arange(B, dtype=torch.int32, device=dev)
+
     def launch(r, stream):
-        mla.bf16_decode(inp.q_lat, inp.q_rope, reps[r], inp.page_table, inp.seq_lens,
+        if step is not None:
+            mla.bf16_write(step.c_kv, step.k_rope, seq_ids, step.pos, inp.page_table, reps[r],
+                           stream=stream)
+        mla.bf16_decode(inp.q_lat, inp.q_rope, reps[r], inp.page_table, lens,
                         synth.SOFTMAX_SCALE, out=out, lse=lse, workspace=ws, stream=stream)
 
     ev_ms = []
@@ -492,16 +501,20 @@ def time_bf16_decode(args, inp, B, H):
     return float(np.mean(ev_ms)) * 1e3, nbytes
 
 
-def paired_bf16(args, wl, inp, t_lowbit_us, lowbit_cache_bytes):
+def paired_bf16(args, wl, inp, t_lowbit_us, lowbit_cache_bytes, step=None):
     """Figure 5(b) / Table 9 of the pages: the low-bit decode's latency against
-    a paired BF16-cache decode of the same batch, delta = t_lowbit / t_bf16 - 1."""
-    lens = inp.seq_lens.cpu().tolist()
-    t_bf16, nbytes = time_bf16_decode(args, inp, wl.B, wl.H)
+    a paired BF16-cache decode of the same batch, delta = t_lowbit / t_bf16 - 1
+    (for a serving step: write + decode on both sides)."""
+    lens = (inp.seq_lens if step is None else step.seq_lens).cpu().tolist()
+    t_bf16, nbytes = time_bf16_decode(args, inp, wl.B, wl.H, step)
     bw = bf16_algorithmic_bytes(lens, wl.H) / (t_bf16 / 1e6) / 1e9
     print(f"[bench] paired BF16 cache: {t_bf16:.1f} us/step events "
           f"({bw:.0f} GB/s algorithmic)", file=sys.stderr, flush=True)
-    tr = measured_traffic(wl.name, "bf16_decode")
-    return {"kernel": "mla_bf16_decode: decode_kernel<BF16 pages> + combine_kernel",
+    tr = measured_traffic(wl.name, "bf16_decode") if step is None else None
+    return {"kernel": ("mla_bf16_decode: decode_kernel<BF16 pages> + combine_kernel"
+                       if step is None else
+                       "mla_bf16_write + mla_bf16_decode: write_bf16_kernel + decode_kernel<BF16 "
+                       "pages> + combine_kernel"),
             "event_us_mean": round(t_bf16, 2), "hbm_frac": round(bw / PEAK_HBM_GBS, 4),
             "traffic": tr["bytes_per_call"] if tr else None,
             "delta_pct": round((t_lowbit_us / t_bf16 - 1.0) * 100.0, 2),
