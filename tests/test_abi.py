@@ -176,3 +176,28 @@ def test_decode_mq_validation_errors():
     assert call(q_lat=None) == binding.EINVAL
     assert call(ws_bytes=16) == binding.EWORKSPACE
     assert call(B=0) == binding.OK
+
+
+def test_binding_shape_checks():
+    """The binding rejects mismatched shapes before it touches the GPU."""
+    import torch
+    bf = torch.bfloat16
+    i32 = torch.int32
+    pt = torch.zeros(2, 4, dtype=i32)
+    sl = torch.zeros(2, dtype=i32)
+    with pytest.raises(ValueError):  # q_lat must be 4-D for the multi-query call
+        mla.decode_mq(mla.C4R4, torch.zeros(2, 16, 512, dtype=bf), torch.zeros(2, 16, 64, dtype=bf),
+                      None, pt, sl, None, None, 0.1)
+    with pytest.raises(ValueError):  # q_rope shape differs from q_lat's
+        mla.decode_mq(mla.C4R4, torch.zeros(2, 2, 16, 512, dtype=bf),
+                      torch.zeros(2, 1, 16, 64, dtype=bf), None, pt, sl, None, None, 0.1)
+    with pytest.raises(ValueError):  # BF16 pages must be [num_pages, 64, 576]
+        mla.bf16_decode(torch.zeros(2, 16, 512, dtype=bf), torch.zeros(2, 16, 64, dtype=bf),
+                        torch.zeros(4, 64, 512, dtype=bf), pt, sl, 0.1)
+    with pytest.raises(ValueError):  # token rows must be [n, 512] / [n, 64]
+        mla.bf16_write(torch.zeros(3, 512, dtype=bf), torch.zeros(3, 32, dtype=bf),
+                       torch.zeros(3, dtype=i32), torch.zeros(3, dtype=i32), pt,
+                       torch.zeros(4, 64, 576, dtype=bf))
+    with pytest.raises(ValueError):  # QDQ outputs must match the inputs
+        mla.qdq(mla.C4R4, torch.zeros(3, 512, dtype=bf), torch.zeros(3, 64, dtype=bf),
+                out_c=torch.zeros(2, 512, dtype=bf))
