@@ -324,7 +324,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u4/u2 codes, f16 MFMA, f32 accumulate",
+        "dtype": ("u4 codes (C4R4)" if wl.c_bits == 4 else "u2 content / u4 RoPE codes (C2R4)")
+                 + ", f16 MFMA, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": wl.desc + (f", s_q={args.sq}" if args.sq > 1 else ""),
                    "B": wl.B, "H": wl.H, "s_q": args.sq,
