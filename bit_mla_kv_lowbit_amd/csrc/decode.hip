@@ -548,7 +548,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float mref[WAVES * 16];
   __shared__ __attribute__((aligned(16))) int flag[WAVES];
   __shared__ __attribute__((aligned(16))) float lsum[WAVES * 16];
-  __shared__ int pids[MAX_ITEMS];  // physical pages of this workgroup's packed items
+  // physical pages of the first 256 items (a longer range, where the split
+  // plan makes one, reads the rest from the page table with scalar loads)
+  __shared__ int pids[256];
   __shared__ __attribute__((aligned(16))) half8 q_lds[CB == 16 ? Q_LDS * 64 : 1];
 
   // All scalar arguments are read up front (one round trip, not one per first
@@ -737,7 +739,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   const PageLds pl{pbuf, mref, flag};
   if (n_it > 0) {
     for (int k = 0;; ++k) {
-      const int pid_next = pids[max(0, min(k + 1, n_pk - 1))];  // read ahead of its use
+      const int kn = max(0, min(k + 1, n_pk - 1));
+      const int pid_next = kn < 256 ? pids[kn] : *(const_i32*)(ptab_b + it0 + kn);  // read ahead
       const float4v S = score_item(regs, k);
       // From the softmax to the end of the PV product the wave's instructions
       // take precedence over those of the other workgroup's wave on the SIMD
@@ -881,15 +884,29 @@ __global__ __launch_bounds__(SL * CL) void combine_kernel(DecodeArgs a) {
 
 SplitPlan plan_splits(int B, int H, int max_pages) {
   // two 4-wave workgroups per CU (256 CUs) when the batch is small; enough
-  // workgroups that none takes more than MAX_ITEMS pages: the page weight is
+  // workgroups that none takes more than a cap of pages: the page weight is
   // at most 2 max_pages + 16 (the sink page +1, at most 5 pages of a
   // 256-token window +3 each) and every page weighs at least 2, so a share
-  // spans fewer than (max_pages + 8) / n + 1 pages
+  // spans fewer than (max_pages + 8) / n + 1 pages. The cap is 256 pages;
+  // where it needs more splits than one round of 512 workgroups holds, a
+  // single round with up to MAX_ITEMS pages per workgroup is used if that
+  // suffices, else the split count is rounded up to whole rounds (no round
+  // that leaves most CUs idle).
   const int n_hb = H / 16;
   const int64_t base = (int64_t)(B > 0 ? B : 1) * n_hb;
-  int n = (int)(512 / base);
-  const int need = (max_pages + 8 + (MAX_ITEMS - 4) - 1) / (MAX_ITEMS - 4);
-  if (n < need) n = need;
+  const int n_round = (int)(512 / base);  // splits that make one full round
+  int n = n_round;
+  const int need256 = (max_pages + 8 + (256 - 4) - 1) / (256 - 4);
+  const int need_max = (max_pages + 8 + (MAX_ITEMS - 4) - 1) / (MAX_ITEMS - 4);
+  if (need256 > n) {
+    if (n >= 1 && need_max <= n) {
+      // one round, longer ranges
+    } else if (n >= 1) {
+      n = (need256 + n - 1) / n * n;
+    } else {
+      n = need256;
+    }
+  }
   if (n > max_pages) n = max_pages;
   if (n < 1) n = 1;
   SplitPlan sp;

@@ -51,7 +51,7 @@ struct DecodeArgs {
 // Upper bound on partials per sequence that the combine kernel merges.
 constexpr int MAX_SPLITS = 2048;
 // Upper bound on work items (pages or protected-token chunks) per workgroup.
-constexpr int MAX_ITEMS = 256;
+constexpr int MAX_ITEMS = 512;
 
 struct SplitPlan {
   int n_split;

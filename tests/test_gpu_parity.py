@@ -482,3 +482,45 @@ def test_protection_settings(c_bits, n_sink, n_local):
     r2, rl2 = oracle.decode(oc, synth.SOFTMAX_SCALE, u16(inp.q_lat), u16(inp.q_rope), op2,
                             pt.numpy(), lens_new.numpy(), osink, olocal)
     assert_decode_ok(out2, lse2, r2, rl2, label=f"prot step s{n_sink} l{n_local}")
+
+
+def test_ranges_longer_than_256_pages():
+    """B32 H256 (one round of workgroups holds one range per sequence and head
+    block) at 20000 tokens: each workgroup takes a 313-page range, beyond the
+    first 256 page ids its threads stage; packed and BF16 caches."""
+    B, H, L = 32, 256, 20000
+    cfg = _cfg(4)
+    oc = ocfg_of(cfg)
+    print("[case] ranges beyond 256 pages: B32 H256 L20000", flush=True)
+    inp = synth.build_cache_inputs([L] * B, H, seed=77, device=DEV)
+    pages, sink, local = mla.allocate_cache(cfg, B, inp.num_pages, DEV)
+    mla.write(cfg, inp.c_kv, inp.k_rope, inp.seq_idx, inp.pos, inp.seq_lens, inp.page_table,
+              pages, sink, local)
+    out, lse = mla.decode(cfg, inp.q_lat, inp.q_rope, pages, inp.page_table, inp.seq_lens, sink,
+                          local, synth.SOFTMAX_SCALE)
+    p16 = mla.allocate_bf16_cache(inp.num_pages, DEV)
+    mla.bf16_write(inp.c_kv, inp.k_rope, inp.seq_idx, inp.pos, inp.page_table, p16)
+    o16, l16 = mla.bf16_decode(inp.q_lat, inp.q_rope, p16, inp.page_table, inp.seq_lens,
+                               synth.SOFTMAX_SCALE)
+    torch.cuda.synchronize()
+    assert mla.binding.lib() is not None
+    rows = [(b, h) for b in (0, 31) for h in (0, 17, 128, 255)]
+    seqs = [0, 31]
+    mask = torch.zeros(inp.seq_idx.numel(), dtype=torch.bool, device=DEV)
+    for b in seqs:
+        mask |= inp.seq_idx == b
+    sub = synth.CacheInputs(inp.c_kv[mask].cpu(), inp.k_rope[mask].cpu(), inp.seq_idx[mask].cpu(),
+                            inp.pos[mask].cpu(), inp.seq_lens.cpu(), inp.page_table.cpu(),
+                            inp.num_pages, inp.q_lat.cpu(), inp.q_rope.cpu())
+    op, osink, olocal = oracle_cache(oc, sub, B)
+    ref, ref_lse = oracle.decode(oc, synth.SOFTMAX_SCALE, u16(inp.q_lat), u16(inp.q_rope), op,
+                                 inp.page_table.cpu().numpy(), inp.seq_lens.cpu().numpy(), osink,
+                                 olocal, sel=rows)
+    assert_decode_ok(out, lse, ref, ref_lse, rows=rows, label="313-page ranges")
+    ob = np.zeros((inp.num_pages, 64, 576), np.uint16)
+    oracle.bf16_write(oracle.Cfg(), u16(sub.c_kv), u16(sub.k_rope), sub.seq_idx.numpy(),
+                      sub.pos.numpy(), sub.page_table.numpy(), ob)
+    r16, rl16 = oracle.bf16_decode(oracle.Cfg(), synth.SOFTMAX_SCALE, u16(inp.q_lat),
+                                   u16(inp.q_rope), ob, inp.page_table.cpu().numpy(),
+                                   inp.seq_lens.cpu().numpy(), sel=rows)
+    assert_decode_ok(o16, l16, r16, rl16, rows=rows, label="313-page ranges, bf16")
