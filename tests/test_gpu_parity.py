@@ -92,6 +92,47 @@ def test_writer_signed_zero_ties(c_bits):
 
 
 @pytest.mark.parametrize("c_bits", [4, 2])
+def test_writer_exact_ties(c_bits):
+    """Groups whose code quotients, fp16 scale or fp16 zero point lie exactly on
+    a rounding tie (hand-derived results in tests/golden/quant_ties.txt): the
+    GPU writer's pages are bit-identical to the oracle's and hold the golden
+    codes and (scale, zero) pairs, ties going to the even value."""
+    from tests import golden_ties
+    groups = golden_ties.load()
+    gs = [g for g in groups if g.bits == c_bits]
+    r4 = [g for g in groups if g.bits == 4]
+    cfg = _cfg(c_bits)
+    n = 64
+    content = [[gs[(i + t) % len(gs)] for i in range(16)] for t in range(n)]
+    rope = [[r4[t % len(r4)], r4[(t + 1) % len(r4)]] for t in range(n)]
+    c = np.stack([np.concatenate([g.x for g in row]) for row in content])
+    r = np.stack([np.concatenate([g.x for g in row]) for row in rope])
+    inp = synth.build_cache_inputs([n], 16, seed=8, device="cpu")
+    inp.c_kv = torch.from_numpy(c).to(torch.bfloat16)
+    inp.k_rope = torch.from_numpy(r).to(torch.bfloat16)
+    print(f"[case] writer exact ties c_bits={c_bits}", flush=True)
+    pages, sink, local = gpu_cache(cfg, inp, 1, canary=0x3C)
+    torch.cuda.synchronize()
+    op, osink, olocal = oracle_cache(ocfg_of(cfg), inp, 1, canary=0x3C)
+    gp = pages.cpu().numpy()
+    assert np.array_equal(gp, op)
+    assert np.array_equal(u16(sink), osink)
+    assert np.array_equal(u16(local), olocal)
+    oc = ocfg_of(cfg)
+    off = oracle.page_regions(oc)
+    pid = int(inp.page_table[0, 0])
+    for t in range(n):
+        codes = golden_ties.codes_from_page(gp[pid], t, c_bits, off[0])
+        sz = gp[pid, off[2] + 64 * t: off[2] + 64 * (t + 1)].copy().view("<u2").reshape(16, 2)
+        for gi, g in enumerate(content[t]):
+            assert np.array_equal(codes[gi], g.codes), (t, gi, g.name)
+            assert (int(sz[gi, 0]), int(sz[gi, 1])) == (g.s16, g.z16), (t, gi, g.name)
+        rsz = gp[pid, off[3] + 8 * t: off[3] + 8 * (t + 1)].copy().view("<u2").reshape(2, 2)
+        for gi, g in enumerate(rope[t]):
+            assert (int(rsz[gi, 0]), int(rsz[gi, 1])) == (g.s16, g.z16), (t, gi, g.name)
+
+
+@pytest.mark.parametrize("c_bits", [4, 2])
 @pytest.mark.parametrize("H", [16, 128])
 def test_decode_edge_lengths(c_bits, H):
     cfg = _cfg(c_bits)
