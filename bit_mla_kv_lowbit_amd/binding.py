@@ -140,8 +140,59 @@ def _check(fn: str, rc: int):
 
 
 def _want(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _expect(t, name, dtype, shape):
+    """t must be a tensor of `dtype` and exactly `shape` (None: any size).
+    The C ABI sees only pointers, so these checks are what keeps a kernel
+    from reading or writing past a caller's buffer."""
+    _want(t, dtype, name)
+    if len(t.shape) != len(shape) or any(
+            want is not None and int(got) != want for got, want in zip(t.shape, shape)):
+        raise ValueError(f"{name} must have shape {tuple('*' if x is None else x for x in shape)}"
+                         f", got {tuple(t.shape)}")
+
+
+def _check_cache(cfg: "Config", B: int, pages, sink, local, page_table, seq_lens):
+    """Packed pages uint8 [num_pages, page_bytes]; sink / local bf16
+    [B, n_sink | n_local, d_c + d_r] (unused, may be None, when the count is 0);
+    page_table int32 [B, max_pages]; seq_lens int32 [B]."""
+    pb = page_bytes(cfg)
+    if pb == 0:
+        c = cfg.c()
+        raise MlaLowbitError("mla_lowbit_check_config", lib().mla_lowbit_check_config(ctypes.byref(c)))
+    _expect(pages, "pages", torch.uint8, (None, pb))
+    D = cfg.d_c + cfg.d_r
+    if cfg.n_sink > 0:
+        _expect(sink, "sink", torch.bfloat16, (B, cfg.n_sink, D))
+    if cfg.n_local > 0:
+        _expect(local, "local", torch.bfloat16, (B, cfg.n_local, D))
+    _expect(page_table, "page_table", torch.int32, (B, None))
+    if page_table.shape[1] < 1:
+        raise ValueError("page_table needs at least one column")
+    _expect(seq_lens, "seq_lens", torch.int32, (B,))
+
+
+def _outputs(out, lse, shape, dev):
+    """Allocate or check out (bf16 [*shape, d_c]) and lse (fp32 shape)."""
+    if out is None:
+        out = torch.empty(*shape, 512, dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty(*shape, dtype=torch.float32, device=dev)
+    _expect(out, "out", torch.bfloat16, (*shape, 512))
+    _expect(lse, "lse", torch.float32, tuple(shape))
+    return out, lse
+
+
+def _workspace(workspace, need, dev):
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _want(workspace, torch.uint8, "workspace")
+    return workspace
 
 
 def allocate_cache(cfg: Config, B: int, num_pages: int, device="cuda"):
@@ -157,15 +208,15 @@ def allocate_cache(cfg: Config, B: int, num_pages: int, device="cuda"):
 def write(cfg: Config, c_kv, k_rope, seq_idx, pos, seq_lens, page_table, pages, sink, local,
           stream=None) -> None:
     """mla_lowbit_write: quantize + pack every token, keep BF16 copies of protected ones."""
-    _want(c_kv, torch.bfloat16, "c_kv")
-    _want(k_rope, torch.bfloat16, "k_rope")
-    for n, t in (("seq_idx", seq_idx), ("pos", pos), ("seq_lens", seq_lens),
-                 ("page_table", page_table)):
-        _want(t, torch.int32, n)
+    _want(seq_idx, torch.int32, "seq_idx")
     n = int(seq_idx.numel())
-    if c_kv.shape != (n, cfg.d_c) or k_rope.shape != (n, cfg.d_r) or pos.numel() != n:
-        raise ValueError("c_kv / k_rope / pos do not match seq_idx")
+    _expect(seq_idx, "seq_idx", torch.int32, (n,))
+    _expect(c_kv, "c_kv", torch.bfloat16, (n, cfg.d_c))
+    _expect(k_rope, "k_rope", torch.bfloat16, (n, cfg.d_r))
+    _expect(pos, "pos", torch.int32, (n,))
+    _want(page_table, torch.int32, "page_table")
     B, max_pages = page_table.shape
+    _check_cache(cfg, B, pages, sink, local, page_table, seq_lens)
     c = cfg.c()
     rc = lib().mla_lowbit_write(ctypes.byref(c), n, _ptr(c_kv), _ptr(k_rope), _ptr(seq_idx),
                                 _ptr(pos), _ptr(seq_lens), _ptr(page_table), B, max_pages,
@@ -177,17 +228,16 @@ def decode(cfg: Config, q_lat, q_rope, pages, page_table, seq_lens, sink, local,
            out=None, lse=None, workspace=None, stream=None):
     """mla_lowbit_decode. Returns (out bf16 [B,H,d_c], lse fp32 [B,H])."""
     _want(q_lat, torch.bfloat16, "q_lat")
-    _want(q_rope, torch.bfloat16, "q_rope")
+    if q_lat.dim() != 3:
+        raise ValueError("q_lat must be [B, H, d_c]")
     B, H, _ = q_lat.shape
+    _expect(q_lat, "q_lat", torch.bfloat16, (B, H, cfg.d_c))
+    _expect(q_rope, "q_rope", torch.bfloat16, (B, H, cfg.d_r))
+    _check_cache(cfg, B, pages, sink, local, page_table, seq_lens)
     max_pages = page_table.shape[1]
     dev = q_lat.device
-    if out is None:
-        out = torch.empty(B, H, cfg.d_c, dtype=torch.bfloat16, device=dev)
-    if lse is None:
-        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
-    need = decode_workspace_bytes(cfg, B, H, max_pages)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    out, lse = _outputs(out, lse, (B, H), dev)
+    workspace = _workspace(workspace, decode_workspace_bytes(cfg, B, H, max_pages), dev)
     c = cfg.c()
     rc = lib().mla_lowbit_decode(ctypes.byref(c), B, H, float(scale), _ptr(q_lat), _ptr(q_rope),
                                  _ptr(pages), _ptr(page_table), max_pages, _ptr(seq_lens),
@@ -209,19 +259,11 @@ def decode_mq(cfg: Config, q_lat, q_rope, pages, page_table, seq_lens, sink, loc
     B, s_q, H, _ = q_lat.shape
     if q_rope.shape != (B, s_q, H, cfg.d_r):
         raise ValueError("q_rope must be [B, s_q, H, d_r]")
+    _check_cache(cfg, B, pages, sink, local, page_table, seq_lens)
     max_pages = page_table.shape[1]
     dev = q_lat.device
-    if out is not None and out.shape != (B, s_q, H, cfg.d_c):
-        raise ValueError("out must be [B, s_q, H, d_c]")
-    if lse is not None and lse.shape != (B, s_q, H):
-        raise ValueError("lse must be [B, s_q, H]")
-    if out is None:
-        out = torch.empty(B, s_q, H, cfg.d_c, dtype=torch.bfloat16, device=dev)
-    if lse is None:
-        lse = torch.empty(B, s_q, H, dtype=torch.float32, device=dev)
-    if workspace is None:
-        need = decode_workspace_bytes(cfg, B, s_q * H, max_pages)
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    out, lse = _outputs(out, lse, (B, s_q, H), dev)
+    workspace = _workspace(workspace, decode_workspace_bytes(cfg, B, s_q * H, max_pages), dev)
     c = cfg.c()
     rc = lib().mla_lowbit_decode_mq(ctypes.byref(c), B, s_q, H, float(scale), _ptr(q_lat),
                                     _ptr(q_rope), _ptr(pages), _ptr(page_table), max_pages,
@@ -235,17 +277,22 @@ def decode_mq(cfg: Config, q_lat, q_rope, pages, page_table, seq_lens, sink, loc
 
 def write_decode(cfg: Config, c_kv, k_rope, pos, q_lat, q_rope, pages, page_table, seq_lens,
                  sink, local, scale: float, out=None, lse=None, workspace=None, stream=None):
-    """mla_lowbit_write_decode: one new token per sequence, then decode."""
+    """mla_lowbit_write_decode: one new token per sequence (c_kv [B, d_c], k_rope
+    [B, d_r], pos [B]), then decode."""
+    _want(q_lat, torch.bfloat16, "q_lat")
+    if q_lat.dim() != 3:
+        raise ValueError("q_lat must be [B, H, d_c]")
     B, H, _ = q_lat.shape
+    _expect(q_lat, "q_lat", torch.bfloat16, (B, H, cfg.d_c))
+    _expect(q_rope, "q_rope", torch.bfloat16, (B, H, cfg.d_r))
+    _expect(c_kv, "c_kv", torch.bfloat16, (B, cfg.d_c))
+    _expect(k_rope, "k_rope", torch.bfloat16, (B, cfg.d_r))
+    _expect(pos, "pos", torch.int32, (B,))
+    _check_cache(cfg, B, pages, sink, local, page_table, seq_lens)
     max_pages = page_table.shape[1]
     dev = q_lat.device
-    if out is None:
-        out = torch.empty(B, H, cfg.d_c, dtype=torch.bfloat16, device=dev)
-    if lse is None:
-        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
-    need = decode_workspace_bytes(cfg, B, H, max_pages)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    out, lse = _outputs(out, lse, (B, H), dev)
+    workspace = _workspace(workspace, decode_workspace_bytes(cfg, B, H, max_pages), dev)
     c = cfg.c()
     rc = lib().mla_lowbit_write_decode(ctypes.byref(c), B, H, float(scale), _ptr(c_kv),
                                        _ptr(k_rope), _ptr(pos), _ptr(q_lat), _ptr(q_rope),
@@ -294,15 +341,14 @@ def allocate_bf16_cache(num_pages: int, device="cuda", d_c: int = 512, d_r: int 
 
 def bf16_write(c_kv, k_rope, seq_idx, pos, page_table, pages, stream=None) -> None:
     """mla_bf16_write: copy token rows into the BF16 paged cache."""
-    _want(c_kv, torch.bfloat16, "c_kv")
-    _want(k_rope, torch.bfloat16, "k_rope")
-    for n, t in (("seq_idx", seq_idx), ("pos", pos), ("page_table", page_table)):
-        _want(t, torch.int32, n)
+    _want(seq_idx, torch.int32, "seq_idx")
     n = int(seq_idx.numel())
-    if c_kv.shape != (n, 512) or k_rope.shape != (n, 64) or pos.numel() != n:
-        raise ValueError("c_kv / k_rope / pos do not match seq_idx")
-    if pages.dtype != torch.bfloat16 or pages.dim() != 3 or pages.shape[1:] != (64, 576):
-        raise ValueError("pages must be bf16 [num_pages, 64, 576]")
+    _expect(seq_idx, "seq_idx", torch.int32, (n,))
+    _expect(c_kv, "c_kv", torch.bfloat16, (n, 512))
+    _expect(k_rope, "k_rope", torch.bfloat16, (n, 64))
+    _expect(pos, "pos", torch.int32, (n,))
+    _expect(pages, "pages", torch.bfloat16, (None, 64, 576))
+    _expect(page_table, "page_table", torch.int32, (None, None))
     B, max_pages = page_table.shape
     rc = lib().mla_bf16_write(n, _ptr(c_kv), _ptr(k_rope), _ptr(seq_idx), _ptr(pos),
                               _ptr(page_table), B, max_pages, _ptr(pages), _stream(stream))
@@ -319,17 +365,13 @@ def bf16_decode(q_lat, q_rope, pages, page_table, seq_lens, scale: float, out=No
     B, H, d_c = q_lat.shape
     if q_rope.shape != (B, H, 64):
         raise ValueError("q_rope must be [B, H, 64]")
-    if pages.dtype != torch.bfloat16 or pages.dim() != 3 or pages.shape[1:] != (64, 576):
-        raise ValueError("pages must be bf16 [num_pages, 64, 576]")
+    _expect(pages, "pages", torch.bfloat16, (None, 64, 576))
+    _expect(page_table, "page_table", torch.int32, (B, None))
+    _expect(seq_lens, "seq_lens", torch.int32, (B,))
     max_pages = page_table.shape[1]
     dev = q_lat.device
-    if out is None:
-        out = torch.empty(B, H, d_c, dtype=torch.bfloat16, device=dev)
-    if lse is None:
-        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
-    if workspace is None:
-        workspace = torch.empty(max(bf16_decode_workspace_bytes(B, H, max_pages), 16),
-                                dtype=torch.uint8, device=dev)
+    out, lse = _outputs(out, lse, (B, H), dev)
+    workspace = _workspace(workspace, bf16_decode_workspace_bytes(B, H, max_pages), dev)
     rc = lib().mla_bf16_decode(B, H, float(scale), _ptr(q_lat), _ptr(q_rope), _ptr(pages),
                                _ptr(page_table), max_pages, _ptr(seq_lens), _ptr(out), _ptr(lse),
                                _ptr(workspace), workspace.numel() * workspace.element_size(),

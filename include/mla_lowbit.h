@@ -8,9 +8,9 @@
  *   - the cache keeps the content latent c_kv and the decoupled RoPE key
  *     k_rope as low-bit codes: INT4 + INT4 ("C4R4") or INT2 content with an
  *     INT4 RoPE key ("C2R4") (abstract);
- *   - a fused writer produces a packed copy of every incoming token and keeps
- *     the pre-quantization BF16 values of protected sink and recent tokens in
- *     dedicated buffers (Figure 8 caption; Figure 3 caption);
+ *   - a fused writer packs every incoming token; sink and recent tokens also
+ *     keep their original unquantized BF16 rows, in buffers of their own
+ *     (Figure 8 caption; Figure 3 caption);
  *   - the protection policy is sink4/local128 (Figure 5 and Table 9 captions);
  *   - attention unpacks and dequantizes inside the kernel, reads BF16 values
  *     for protected tokens, shares one reconstructed content tile between the
@@ -110,7 +110,7 @@ size_t mla_lowbit_decode_workspace_bytes(const mla_lowbit_config* cfg, int B, in
 
 /*
  * Fused writer (Figure 8 caption: a packed copy for every incoming token, plus
- * the pre-quantization BF16 values of protected tokens).
+ * the unquantized BF16 row of each protected token).
  *   n_tokens    tokens to write (>= 0; 0 is a no-op)
  *   c_kv        bf16 [n_tokens, d_c]   content latents
  *   k_rope      bf16 [n_tokens, d_r]   RoPE keys, already rotated
@@ -124,8 +124,12 @@ size_t mla_lowbit_decode_workspace_bytes(const mla_lowbit_config* cfg, int B, in
  * Each (seq, pos) may appear at most once per call, so no ring slot is
  * written twice by one call. A token whose seq_idx is outside [0, B) or whose
  * pos is outside [0, max_pages * page_size) is dropped (nothing is written);
- * page_table entries must name pages that exist (not checked on the device). A token leaving the recent window needs no
- * call: its packed copy already exists (Figure 8 caption).
+ * page_table entries must name pages that exist (not checked on the device).
+ * A token leaving the recent window needs no call: its packed copy already
+ * exists (Figure 8 caption).
+ * Precondition: every c_kv / k_rope value lies in the fp16 range
+ * (|x| <= 65504), since each group's zero point and scale are stored in fp16;
+ * a group beyond it gets an infinite zero or scale and undefined codes.
  */
 int mla_lowbit_write(const mla_lowbit_config* cfg, int n_tokens, const void* c_kv,
                      const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
@@ -151,6 +155,11 @@ int mla_lowbit_write(const mla_lowbit_config* cfg, int n_tokens, const void* c_k
  *                mla_lowbit_decode_workspace_bytes(cfg, B, H, max_pages) bytes
  * The sequence is split into page ranges processed in parallel and merged by
  * their log-sum-exp (one global softmax, Figure 8 caption).
+ * Precondition (fp16 inside the kernel): q_lat, q_rope and the BF16 rows of
+ * the sink / local buffers are converted to fp16 for the MFMA products. That
+ * is exact for bf16 values with 2^-14 <= |x| <= 65504 (and for 0); larger
+ * magnitudes overflow to infinity (undefined results), and smaller ones
+ * become fp16 subnormals that keep only the bits at or above 2^-24.
  */
 int mla_lowbit_decode(const mla_lowbit_config* cfg, int B, int H, float softmax_scale,
                       const void* q_lat, const void* q_rope, const void* pages,

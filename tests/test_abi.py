@@ -201,3 +201,108 @@ def test_binding_shape_checks():
     with pytest.raises(ValueError):  # QDQ outputs must match the inputs
         mla.qdq(mla.C4R4, torch.zeros(3, 512, dtype=bf), torch.zeros(3, 64, dtype=bf),
                 out_c=torch.zeros(2, 512, dtype=bf))
+
+
+def _bad_shape(fn, *a, match="must have shape", **k):
+    with pytest.raises(ValueError, match=match):
+        fn(*a, **k)
+
+
+def test_binding_checks_every_tensor_of_decode_and_write():
+    """Every tensor a call hands to the C ABI is checked for dtype and shape on
+    the host first (CPU tensors here: a check that passed would go on to the
+    device-pointer check, whose message differs)."""
+    import torch
+    bf, i32, u8, f32 = torch.bfloat16, torch.int32, torch.uint8, torch.float32
+    cfg = mla.C4R4
+    B, H, P = 2, 16, 4
+    good = dict(q_lat=torch.zeros(B, H, 512, dtype=bf), q_rope=torch.zeros(B, H, 64, dtype=bf),
+                pages=torch.zeros(8, 23040, dtype=u8), page_table=torch.zeros(B, P, dtype=i32),
+                seq_lens=torch.zeros(B, dtype=i32), sink=torch.zeros(B, 4, 576, dtype=bf),
+                local=torch.zeros(B, 128, 576, dtype=bf))
+
+    def dec(**over):
+        a = dict(good, **over)
+        return mla.decode(cfg, a["q_lat"], a["q_rope"], a["pages"], a["page_table"],
+                          a["seq_lens"], a["sink"], a["local"], 0.1, out=a.get("out"),
+                          lse=a.get("lse"), workspace=a.get("workspace"))
+
+    # all shapes right: the first failure is the device check of the first pointer
+    with pytest.raises(ValueError, match="GPU"):
+        dec(out=torch.zeros(B, H, 512, dtype=bf), lse=torch.zeros(B, H, dtype=f32),
+            workspace=torch.zeros(16, dtype=u8))
+    _bad_shape(dec, q_rope=torch.zeros(B, H, 32, dtype=bf))
+    _bad_shape(dec, q_rope=torch.zeros(B, H + 16, 64, dtype=bf))
+    _bad_shape(dec, pages=torch.zeros(8, 14848, dtype=u8))            # C2R4 pages for C4R4
+    _bad_shape(dec, page_table=torch.zeros(B + 1, P, dtype=i32))
+    _bad_shape(dec, seq_lens=torch.zeros(B - 1, dtype=i32))
+    _bad_shape(dec, sink=torch.zeros(B, 2, 576, dtype=bf))
+    _bad_shape(dec, local=torch.zeros(B - 1, 128, 576, dtype=bf))
+    _bad_shape(dec, out=torch.zeros(B, H, 256, dtype=bf))
+    _bad_shape(dec, lse=torch.zeros(B, H + 1, dtype=f32))
+    with pytest.raises(TypeError):
+        dec(lse=torch.zeros(B, H, dtype=bf))
+    with pytest.raises(TypeError):
+        dec(seq_lens=torch.zeros(B, dtype=torch.int64))
+    with pytest.raises(TypeError):
+        dec(q_rope=torch.zeros(B, H, 64, dtype=torch.float16))
+    with pytest.raises(TypeError):
+        dec(pages=torch.zeros(8, 23040 // 2, dtype=torch.int16))
+    with pytest.raises(TypeError):
+        dec(sink=None)
+
+    def wd(**over):
+        a = dict(good, c_kv=torch.zeros(B, 512, dtype=bf), k_rope=torch.zeros(B, 64, dtype=bf),
+                 pos=torch.zeros(B, dtype=i32))
+        a.update(over)
+        return mla.write_decode(cfg, a["c_kv"], a["k_rope"], a["pos"], a["q_lat"], a["q_rope"],
+                                a["pages"], a["page_table"], a["seq_lens"], a["sink"],
+                                a["local"], 0.1)
+
+    _bad_shape(wd, c_kv=torch.zeros(B + 1, 512, dtype=bf))
+    _bad_shape(wd, k_rope=torch.zeros(B, 32, dtype=bf))
+    _bad_shape(wd, pos=torch.zeros(B + 1, dtype=i32))
+    _bad_shape(wd, seq_lens=torch.zeros(B + 1, dtype=i32))
+    with pytest.raises(TypeError):
+        wd(pos=torch.zeros(B, dtype=torch.int64))
+
+    n = 3
+
+    def wr(**over):
+        a = dict(good, c_kv=torch.zeros(n, 512, dtype=bf), k_rope=torch.zeros(n, 64, dtype=bf),
+                 seq_idx=torch.zeros(n, dtype=i32), pos=torch.zeros(n, dtype=i32))
+        a.update(over)
+        return mla.write(cfg, a["c_kv"], a["k_rope"], a["seq_idx"], a["pos"], a["seq_lens"],
+                         a["page_table"], a["pages"], a["sink"], a["local"])
+
+    with pytest.raises(ValueError, match="GPU"):
+        wr()
+    _bad_shape(wr, pos=torch.zeros(n + 1, dtype=i32))
+    _bad_shape(wr, c_kv=torch.zeros(n, 256, dtype=bf))
+    _bad_shape(wr, seq_lens=torch.zeros(B + 2, dtype=i32))
+    _bad_shape(wr, local=torch.zeros(B, 64, 576, dtype=bf))
+    _bad_shape(wr, pages=torch.zeros(8, 23041, dtype=u8))
+    with pytest.raises(binding.MlaLowbitError):  # unsupported config: refused before shapes
+        mla.decode(mla.Config(group=48), good["q_lat"], good["q_rope"], good["pages"],
+                   good["page_table"], good["seq_lens"], good["sink"], good["local"], 0.1)
+
+
+def test_binding_checks_bf16_and_mq_outputs():
+    import torch
+    bf, i32, f32 = torch.bfloat16, torch.int32, torch.float32
+    B, H = 2, 16
+    pages = torch.zeros(4, 64, 576, dtype=bf)
+    pt = torch.zeros(B, 4, dtype=i32)
+    sl = torch.zeros(B, dtype=i32)
+    q, qr = torch.zeros(B, H, 512, dtype=bf), torch.zeros(B, H, 64, dtype=bf)
+    _bad_shape(mla.bf16_decode, q, qr, pages, torch.zeros(B + 1, 4, dtype=i32), sl, 0.1)
+    _bad_shape(mla.bf16_decode, q, qr, pages, pt, torch.zeros(B + 1, dtype=i32), 0.1)
+    _bad_shape(mla.bf16_decode, q, qr, pages, pt, sl, 0.1, out=torch.zeros(B, H, 64, dtype=bf))
+    _bad_shape(mla.bf16_decode, q, qr, pages, pt, sl, 0.1, lse=torch.zeros(B, dtype=f32))
+    qm, qrm = torch.zeros(B, 2, H, 512, dtype=bf), torch.zeros(B, 2, H, 64, dtype=bf)
+    p8 = torch.zeros(4, 23040, dtype=torch.uint8)
+    sink, local = torch.zeros(B, 4, 576, dtype=bf), torch.zeros(B, 128, 576, dtype=bf)
+    _bad_shape(mla.decode_mq, mla.C4R4, qm, qrm, p8, pt, sl, sink, local, 0.1,
+               out=torch.zeros(B, H, 512, dtype=bf))
+    _bad_shape(mla.decode_mq, mla.C4R4, qm, qrm, p8, pt, torch.zeros(B, 1, dtype=i32), sink,
+               local, 0.1)
