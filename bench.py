@@ -1,9 +1,13 @@
 """Decode throughput of the packed low-bit MLA cache on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v2lite] [--no-cpu]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload serve] [--no-cpu]
 
-A step is one mla_lowbit_decode over one batch of the workload (for the serving
-workload: one mla_lowbit_write_decode). The W warmup steps and the K timed
+The default workload is the largest one-GPU configuration, the serving step:
+B64 H128, lengths uniform in [1024, 131072], one token written per sequence
+and then decoded (mla_lowbit_write_decode). The other workloads (tiny, v2lite,
+v3, c2r4) are selected with --workload. A step is one mla_lowbit_decode over
+one batch of the workload (for the serving workload: one
+mla_lowbit_write_decode). The W warmup steps and the K timed
 steps are each captured as one HIP graph; the timed region is one replay of
 the K-step graph (--eager launches every step from Python instead). Inputs are
 resident in HBM when timing starts. Step k uses cache copy k mod R, with R
@@ -85,7 +89,8 @@ def measured_traffic(workload: str, prefix: str = "decode"):
         return {"bytes_per_call": int(float(kv["traffic_bytes_per_call"])),
                 "fetch_bytes": int(float(kv["fetch_bytes_per_call"])),
                 "write_bytes": int(float(kv["write_bytes_per_call"])),
-                "copy_calibration": float(kv["fetch_scale"])}
+                "copy_calibration": float(kv["fetch_scale"]),
+                "write_calibration": float(kv.get("write_scale", "1.0"))}
     except (KeyError, ValueError):
         return None
 
@@ -166,7 +171,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="v2lite")
+    ap.add_argument("--workload", default="serve")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true",
@@ -285,8 +290,14 @@ def main():
              "frac": round(bw / PEAK_HBM_GBS, 4)} if hbm_bound else
             {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_MFMA_TFLOPS,
              "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_TFLOPS, 4)})
-    tr = measured_traffic(args.workload) if step is None else None
+    tr = measured_traffic(args.workload) if args.sq == 1 else None
     roof["traffic"] = tr["bytes_per_call"] if tr else None
+    roof["traffic_source"] = (
+        f"profiles/decode_traffic_{args.workload}.txt: rocprofv3 FETCH_SIZE and WRITE_SIZE "
+        f"passes over the same call on the same kernel sources (hash-checked), fetch scaled "
+        f"x{tr['copy_calibration']:.4f} and write x{tr['write_calibration']:.4f} by what the "
+        f"counters read for a 512 MiB copy kernel; not measured in this run"
+        if tr else "null: no counter summary taken on these kernel sources")
     roof["kernel"] = ("mla_lowbit_decode: decode_kernel + combine_kernel"
                       if step is None else
                       "mla_lowbit_write_decode: write_kernel + decode_kernel + combine_kernel")
@@ -351,6 +362,13 @@ def cpu_baseline(cfg, wl, inp, step, out, lse, lens, budget_s):
     import synth
 
     oc = oracle.Cfg(c_bits=wl.c_bits)
+    # one OpenMP thread per core this process may run on, capped by the
+    # thread count the environment grants (OMP_NUM_THREADS), if it sets one
+    n_affinity = len(os.sched_getaffinity(0))
+    n_threads = n_affinity
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        n_threads = max(1, min(n_threads, int(os.environ["OMP_NUM_THREADS"])))
+    oracle.set_num_threads(n_threads)
     u16 = lambda t: t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
     pt = inp.page_table.cpu().numpy()
     pre = inp.seq_lens.cpu().numpy()
@@ -396,24 +414,27 @@ def cpu_baseline(cfg, wl, inp, step, out, lse, lens, budget_s):
                 break
         passes += 1
     tok_seq = int(sum(final[d] for d in done))
-    cpu = {"value": round(n_tok / spent, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+    cpu = {"value": round(n_tok / spent, 1), "unit": "tokens/s", "cores": n_threads,
            "kind": "oracle",
            "sample": f"{len(done)} of {wl.B} sequences ({tok_seq} cache tokens) x all {wl.H} "
                      f"heads, fp64 plain-loop decode, {passes} pass(es), {n_tok} tokens attended "
-                     f"in {spent:.1f} s"}
-    if wl.name == "tiny":
-        # the single-core time of the whole tiny workload, next to the all-core one
-        n_thr = oracle.num_threads()
-        oracle.set_num_threads(1)
-        t0 = time.perf_counter()
-        reps = 0
-        while time.perf_counter() - t0 < min(budget_s, 5.0):
-            oracle.decode(oc, synth.SOFTMAX_SCALE, ql, qr, op, pt, final, osink, olocal,
-                          sel=[(b, h) for b in done for h in range(wl.H)])
-            reps += 1
-        t1 = time.perf_counter()
-        oracle.set_num_threads(n_thr)
-        cpu["single_core_value"] = round(reps * tok_seq / (t1 - t0), 1)
+                     f"in {spent:.1f} s on {n_threads} OpenMP threads (one per core, heads of a "
+                     f"sequence in parallel)",
+           "affinity_cores": n_affinity, "cpu_model": cpu_model()}
+    # the same oracle on one core, over the shortest sampled sequence
+    b1 = done[0]
+    oracle.set_num_threads(1)
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < min(budget_s / 2, 5.0):
+        oracle.decode(oc, synth.SOFTMAX_SCALE, ql, qr, op, pt, final, osink, olocal,
+                      sel=[(b1, h) for h in range(wl.H)])
+        reps += 1
+    t1 = time.perf_counter()
+    oracle.set_num_threads(n_threads)
+    cpu["single_core_value"] = round(reps * int(final[b1]) / (t1 - t0), 1)
+    cpu["single_core_sample"] = (f"sequence {b1} ({int(final[b1])} cache tokens) x all {wl.H} "
+                                 f"heads, {reps} run(s) in {t1 - t0:.1f} s")
     rows = [(b, h) for b in done for h in range(wl.H)]
     ref = np.concatenate([refs[b] for b in done])
     rl = np.concatenate([ref_lse[b] for b in done])
@@ -425,6 +446,19 @@ def cpu_baseline(cfg, wl, inp, step, out, lse, lens, budget_s):
     parity = {"rows": len(rows), "rel_l2": rel, "max_abs_rel": mx, "lse_abs": dl,
               "pass": bool(rel <= 2e-3 and mx <= 1e-2 and dl <= 1e-3)}
     return cpu, parity
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def copy_bandwidth(nbytes=1 << 30, reps=5):
