@@ -13,7 +13,10 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_lowbit.so")
 
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH, ESCRATCH = 0, -1, -2, -3, -4, -5
+
+# static device scratch of mla_lowbit_decode_noalloc (MLA_LOWBIT_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MlaLowbitError(RuntimeError):
@@ -78,6 +81,9 @@ def lib() -> ctypes.CDLL:
         L.mla_lowbit_write_decode.argtypes = [P, i32, i32, ctypes.c_float, P, P, P, P, P, P, P, i32,
                                               P, P, P, P, P, P, sz, P]
         L.mla_lowbit_write_decode.restype = i32
+        L.mla_lowbit_decode_noalloc.argtypes = [P, i32, i32, ctypes.c_float, P, P, P, P, i32, P,
+                                                P, P, P, P, P]
+        L.mla_lowbit_decode_noalloc.restype = i32
         L.mla_lowbit_decode_mq.argtypes = [P, i32, i32, i32, ctypes.c_float, P, P, P, P, i32,
                                            P, P, P, P, P, P, sz, P]
         L.mla_lowbit_decode_mq.restype = i32
@@ -244,6 +250,32 @@ def decode(cfg: Config, q_lat, q_rope, pages, page_table, seq_lens, sink, local,
                                  _ptr(sink), _ptr(local), _ptr(out), _ptr(lse), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream))
     _check("mla_lowbit_decode", rc)
+    return out, lse
+
+
+def decode_noalloc(cfg: Config, q_lat, q_rope, pages, page_table, seq_lens, sink, local,
+                   scale: float, out, lse, stream=None):
+    """mla_lowbit_decode_noalloc: mla_lowbit_decode with the library's static
+    device scratch in place of a workspace. out (bf16 [B, H, d_c]) and lse
+    (fp32 [B, H]) must be given; the call allocates nothing. Calls that overlap
+    on one GPU share the scratch and race."""
+    _want(q_lat, torch.bfloat16, "q_lat")
+    if q_lat.dim() != 3:
+        raise ValueError("q_lat must be [B, H, d_c]")
+    B, H, _ = q_lat.shape
+    _expect(q_lat, "q_lat", torch.bfloat16, (B, H, cfg.d_c))
+    _expect(q_rope, "q_rope", torch.bfloat16, (B, H, cfg.d_r))
+    _check_cache(cfg, B, pages, sink, local, page_table, seq_lens)
+    if out is None or lse is None:
+        raise ValueError("decode_noalloc allocates nothing: pass out and lse")
+    _expect(out, "out", torch.bfloat16, (B, H, cfg.d_c))
+    _expect(lse, "lse", torch.float32, (B, H))
+    c = cfg.c()
+    rc = lib().mla_lowbit_decode_noalloc(ctypes.byref(c), B, H, float(scale), _ptr(q_lat),
+                                         _ptr(q_rope), _ptr(pages), _ptr(page_table),
+                                         page_table.shape[1], _ptr(seq_lens), _ptr(sink),
+                                         _ptr(local), _ptr(out), _ptr(lse), _stream(stream))
+    _check("mla_lowbit_decode_noalloc", rc)
     return out, lse
 
 

@@ -1,7 +1,10 @@
 // C-ABI entry points (include/mla_lowbit.h): host-side validation, size
-// queries and launches on the caller's stream. Nothing here allocates,
-// synchronizes or keeps state.
+// queries and launches on the caller's stream. Nothing here allocates or
+// synchronizes; the only state is the per-device address of the static
+// scratch array of the no-allocation decode, looked up once.
 #include <math.h>
+
+#include <mutex>
 
 #include "../../include/mla_lowbit.h"
 #include "mla_common.h"
@@ -93,6 +96,34 @@ DecodeArgs make_decode_args(const mla_lowbit_config* cfg, int B, int H, float so
   return a;
 }
 
+
+}  // namespace
+
+// Static workspace of mla_lowbit_decode_noalloc (one copy per GPU, held until
+// the process ends). In host code `scratch` only names the symbol: its device
+// address on the current GPU comes from hipGetSymbolAddress, looked up once
+// per device, and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[MLA_LOWBIT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+
+// Device address of `scratch` on the current device, or null on a HIP error.
+void* scratch_on_current_device() {
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,6 +137,8 @@ const char* mla_lowbit_strerror(int code) {
     case MLA_LOWBIT_EUNSUPPORTED: return "unsupported cache configuration";
     case MLA_LOWBIT_EWORKSPACE: return "workspace smaller than mla_lowbit_decode_workspace_bytes";
     case MLA_LOWBIT_ELAUNCH: return "HIP kernel launch failed";
+    case MLA_LOWBIT_ESCRATCH:
+      return "shape needs more workspace than the 64 MiB static scratch of the no-allocation decode";
     default: return "unknown error code";
   }
 }
@@ -161,6 +194,33 @@ int mla_lowbit_decode(const mla_lowbit_config* cfg, int B, int H, float softmax_
   if (rc || B == 0) return rc;
   DecodeArgs a = make_decode_args(cfg, B, H, softmax_scale, q_lat, q_rope, pages, page_table,
                                   max_pages, seq_lens, sink, local, out, lse, workspace);
+  return launch_decode(a, cfg->c_bits, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_LOWBIT_OK
+             : MLA_LOWBIT_ELAUNCH;
+}
+
+int mla_lowbit_decode_noalloc(const mla_lowbit_config* cfg, int B, int H, float softmax_scale,
+                              const void* q_lat, const void* q_rope, const void* pages,
+                              const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                              const void* sink, const void* local, void* out, float* lse,
+                              void* stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (B < 0 || H <= 0 || H % 16 != 0 || max_pages < 1) return MLA_LOWBIT_EINVAL;
+  if (B == 0) return decode_checks(cfg, B, H, softmax_scale, q_lat, q_rope, pages, page_table,
+                                   max_pages, seq_lens, sink, local, out, lse, nullptr, 0);
+  const size_t need = decode_workspace_bytes(B, H, max_pages);
+  if (need > MLA_LOWBIT_NOALLOC_SCRATCH_BYTES) return MLA_LOWBIT_ESCRATCH;
+  // every other check first, with a stand-in workspace address, so that a bad
+  // argument is reported before the device is touched
+  rc = decode_checks(cfg, B, H, softmax_scale, q_lat, q_rope, pages, page_table, max_pages,
+                     seq_lens, sink, local, out, lse, reinterpret_cast<void*>(uintptr_t{256}),
+                     MLA_LOWBIT_NOALLOC_SCRATCH_BYTES);
+  if (rc) return rc;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return MLA_LOWBIT_ELAUNCH;
+  DecodeArgs a = make_decode_args(cfg, B, H, softmax_scale, q_lat, q_rope, pages, page_table,
+                                  max_pages, seq_lens, sink, local, out, lse, ws);
   return launch_decode(a, cfg->c_bits, static_cast<hipStream_t>(stream)) == hipSuccess
              ? MLA_LOWBIT_OK
              : MLA_LOWBIT_ELAUNCH;

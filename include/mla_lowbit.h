@@ -77,6 +77,12 @@ extern "C" {
 #define MLA_LOWBIT_EUNSUPPORTED (-2) /* configuration outside what the kernels build */
 #define MLA_LOWBIT_EWORKSPACE (-3)   /* workspace smaller than the size query says */
 #define MLA_LOWBIT_ELAUNCH (-4)      /* the HIP runtime reported a launch error */
+#define MLA_LOWBIT_ESCRATCH (-5)     /* shape needs more than the static scratch holds */
+
+/* Size of the static device scratch array that mla_lowbit_decode_noalloc
+ * uses in place of a caller's workspace (one copy per GPU, held until the
+ * process ends). */
+#define MLA_LOWBIT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Cache geometry. Supported: d_c = 512, d_r = 64, c_bits in {4, 2}, r_bits = 4,
  * group = 32, page_size = 64, 0 <= n_sink <= 64, 0 <= n_local <= 256. */
@@ -166,6 +172,30 @@ int mla_lowbit_decode(const mla_lowbit_config* cfg, int B, int H, float softmax_
                       const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                       const void* sink, const void* local, void* out, float* lse,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_lowbit_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops and harnesses that forbid
+ * hipMalloc. Same arguments, kernels and results as mla_lowbit_decode, minus
+ * the workspace: the page-range partials go to a file-scope static device
+ * array of MLA_LOWBIT_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, whose address is
+ * looked up once per device on the first call made with that device current.
+ * The call allocates nothing, through HIP or any library.
+ *   - A shape whose workspace (mla_lowbit_decode_workspace_bytes) exceeds
+ *     MLA_LOWBIT_NOALLOC_SCRATCH_BYTES is refused with MLA_LOWBIT_ESCRATCH
+ *     before anything is launched.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (different streams, no ordering between them) race and
+ *     give undefined results; calls ordered on one stream are safe. Nothing in
+ *     the array needs to start at zero (every partial a call reads was written
+ *     earlier in the same call).
+ *   - `stream` must belong to the current device.
+ */
+int mla_lowbit_decode_noalloc(const mla_lowbit_config* cfg, int B, int H, float softmax_scale,
+                              const void* q_lat, const void* q_rope, const void* pages,
+                              const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                              const void* sink, const void* local, void* out, float* lse,
+                              void* stream);
 
 /*
  * Multi-query decode over the same cache: s_q query tokens per sequence, the

@@ -306,3 +306,20 @@ def test_binding_checks_bf16_and_mq_outputs():
                out=torch.zeros(B, H, 512, dtype=bf))
     _bad_shape(mla.decode_mq, mla.C4R4, qm, qrm, p8, pt, torch.zeros(B, 1, dtype=i32), sink,
                local, 0.1)
+
+
+def test_noalloc_rejects_bad_arguments_before_the_device():
+    c = mla.C4R4.c()
+    L = mla.lib()
+
+    def call(B=2, H=16, max_pages=4, q_lat=_fake(), out=_fake(), scale=0.1):
+        return L.mla_lowbit_decode_noalloc(ctypes.byref(c), B, H, scale, q_lat, _fake(), _fake(),
+                                           _fake(), max_pages, _fake(), _fake(), _fake(), out,
+                                           _fake(), None)
+
+    assert call(H=24) == binding.EINVAL
+    assert call(q_lat=None) == binding.EINVAL
+    assert call(out=_fake(0x10002)) == binding.EINVAL
+    assert call(scale=-1.0) == binding.EINVAL
+    assert call(B=0) == binding.OK
+    assert call(B=64, H=1024, max_pages=4096) == binding.ESCRATCH
