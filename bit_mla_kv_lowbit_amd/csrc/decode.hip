@@ -44,101 +44,13 @@
 // scores, the same tile, softmax, PV and combine.
 #include "mla_common.h"
 #include "mla_kernels.h"
+#include "decode_ops.h"
 
 #include <type_traits>
 
 namespace mla {
 
-constexpr float LN2 = 0.69314718055994530942f;
-constexpr uint32_t MAGIC = 0x64006400u;  // fp16 pair (1024, 1024)
-constexpr int WAVES = 4;                 // wavefronts per workgroup
-constexpr float TAU = 8.f;               // lazy-rescale threshold (log2 units)
-constexpr float M_NONE = -1e30f;         // reference max before any valid token
-
-typedef __attribute__((address_space(3))) short4v lds_short4;
-// read-only data read through the constant address space (scalar loads)
-typedef __attribute__((address_space(4))) const int32_t const_i32;
-
-__device__ __forceinline__ half2v as_h2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
-__device__ __forceinline__ uint32_t as_u32(half2v v) { return __builtin_bit_cast(uint32_t, v); }
-
-// (a & m) | o in one VALU op (the compiler otherwise emits an and plus an or)
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-  return r;
-}
-
-// Raw data one lane loads for one page: sub-block j of its token in each of the
-// 16 content groups and the 2 RoPE groups, and all (scale, zero) words of its
-// token.
-template <int CB>
-struct PageRegs {
-  u32x4 c[CB == 4 ? 4 : 2];  // content code chunks
-  u32x4 sz[4];               // content (s, z) words of groups 0..15
-  u32x2 r;                   // RoPE code words (groups 0, 1)
-  u32x2 rsz;                 // RoPE (s, z) words
-};
-
-// BF16 baseline page: sub-block j of each of the token's 18 groups, raw bf16.
-template <>
-struct PageRegs<16> {
-  u32x4 k[NG_C + NG_R];
-};
-
-// Byte offsets, inside a page, of what one lane (slot, sub-block j) loads,
-// relative to the start of each region (the region starts go in the scalar
-// offset of the buffer loads). The content code chunk m (16 bytes at + 64 m)
-// holds sub-block j of groups 4m .. 4m + 3 (INT4) or 8m .. 8m + 7 (INT2).
-template <int CB>
-struct LaneOffsets {
-  uint32_t c, s, r, rs;
-  __device__ LaneOffsets(int slot, int j) {
-    using G = PageGeom<CB>;
-    c = slot * G::CC + 16 * j;
-    s = slot * G::CS;
-    r = slot * G::RC + 8 * j;
-    rs = slot * G::RS;
-  }
-};
-
-// Buffer descriptor of one physical page (raw byte addressing, range = page;
-// an empty range makes every load return 0 and touch nothing).
-// BF16 page: sub-block j of group g of the row sits at + 64 g (RoPE groups
-// follow the 16 content groups in the row).
-template <>
-struct LaneOffsets<16> {
-  uint32_t c;
-  __device__ LaneOffsets(int slot, int j) : c(slot * PageGeom<16>::ROW + 16 * j) {}
-};
-
-template <int CB>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* pages, int pid,
-                                                            bool any = true) {
-  return __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(pages + (int64_t)pid * PageGeom<CB>::BYTES), (short)0,
-      any ? PageGeom<CB>::BYTES : 0, 0x00020000);
-}
-
-template <int CB>
-__device__ __forceinline__ void load_page(PageRegs<CB>& t, __amdgpu_buffer_rsrc_t rs,
-                                          const LaneOffsets<CB>& o) {
-  if constexpr (CB == 16) {
-#pragma unroll
-    for (int g = 0; g < NG_C + NG_R; ++g)
-      t.k[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.c, 64 * g, 0));
-  } else {
-  using G = PageGeom<CB>;
-#pragma unroll
-  for (int m = 0; m < (CB == 4 ? 4 : 2); ++m)
-    t.c[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.c, G::OFF_CC + 64 * m, 0));
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-    t.sz[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.s, G::OFF_CS + 16 * m, 0));
-  t.r = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.r, G::OFF_RC, 0));
-  t.rsz = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.rs, G::OFF_RS, 0));
-  }
-}
+constexpr int WAVES = 4;  // wavefronts per workgroup
 
 // Scores of the BF16 baseline use bf16 MFMA on Q and the rows as stored
 // (bf16 values travel in half8 bit containers). Its PV product stays in fp16
@@ -163,66 +75,6 @@ __device__ __forceinline__ half8 bf16x8_to_f16x8_rtz(u32x4 w) {
     r[2 * i + 1] = h.y;
   }
   return r;
-}
-
-// Exact codes of channels 8j..8j+7 (pairs (0,1) (2,3) (4,5) (6,7)) of one group
-// from its code word. Codes at bit offsets below 10 are turned into fp16
-// 1024 + 2^o * c with one and-or, then back to c with one exact packed FMA.
-__device__ __forceinline__ half8 codes4(uint32_t wd) {
-  const half2v m1024 = as_h2(0xE400E400u);  // -1024
-  const half2v r16 = as_h2(0x2C002C00u);    // 1/16
-  const half2v m64 = as_h2(0xD400D400u);    // -64
-  const uint32_t t = wd >> 8;
-  const half2v p0 = as_h2(and_or(wd, 0x000F000Fu, MAGIC)) + m1024;
-  const half2v p1 = __builtin_elementwise_fma(as_h2(and_or(wd, 0x00F000F0u, MAGIC)), r16, m64);
-  const half2v p2 = as_h2(and_or(t, 0x000F000Fu, MAGIC)) + m1024;
-  const half2v p3 = __builtin_elementwise_fma(as_h2(and_or(t, 0x00F000F0u, MAGIC)), r16, m64);
-  return (half8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-}
-
-// Same for 2-bit codes: code block e of the word (pairs at bits 8e + 2i, 24 + ... ).
-__device__ __forceinline__ half8 codes2(uint32_t wd, int e) {
-  const uint32_t t = e ? wd >> 8 : wd;
-  const half2v m1024 = as_h2(0xE400E400u);
-  const half2v r4 = as_h2(0x34003400u), m256 = as_h2(0xDC00DC00u);    // 1/4, -256
-  const half2v r16 = as_h2(0x2C002C00u), m64 = as_h2(0xD400D400u);    // 1/16, -64
-  const half2v r64 = as_h2(0x24002400u), m16 = as_h2(0xCC00CC00u);    // 1/64, -16
-  const half2v p0 = as_h2(and_or(t, 0x00030003u, MAGIC)) + m1024;
-  const half2v p1 = __builtin_elementwise_fma(as_h2(and_or(t, 0x000C000Cu, MAGIC)), r4, m256);
-  const half2v p2 = __builtin_elementwise_fma(as_h2(and_or(t, 0x00300030u, MAGIC)), r16, m64);
-  const half2v p3 = __builtin_elementwise_fma(as_h2(and_or(t, 0x00C000C0u, MAGIC)), r64, m16);
-  return (half8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-}
-
-// Codes and (s, z) word of content group g (0..15).
-template <int CB>
-__device__ __forceinline__ half8 content_codes(const PageRegs<CB>& t, int g) {
-  if (CB == 4) return codes4(t.c[g >> 2][g & 3]);
-  return codes2(t.c[g >> 3][(g & 7) >> 1], g & 1);
-}
-template <int CB>
-__device__ __forceinline__ uint32_t content_sz(const PageRegs<CB>& t, int g) {
-  return t.sz[g >> 2][g & 3];
-}
-
-// Reconstructed fp16 values x = c * s + z (one rounding per value).
-__device__ __forceinline__ half8 reconstruct(half8 c, uint32_t sz) {
-  const half2v szh = as_h2(sz);
-  const half2v s2 = __builtin_shufflevector(szh, szh, 0, 0);
-  const half2v z2 = __builtin_shufflevector(szh, szh, 1, 1);
-  half8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const half2v x = __builtin_elementwise_fma((half2v){c[2 * i], c[2 * i + 1]}, s2, z2);
-    r[2 * i] = x.x;
-    r[2 * i + 1] = x.y;
-  }
-  return r;
-}
-
-// z halves of two (s, z) words, packed
-__device__ __forceinline__ uint32_t z_pair(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 // LDS tile of reconstructed content values, 64 token rows x 512 fp16, rows
@@ -258,15 +110,6 @@ struct PvCtx {
   half8 pB[2];
   half8 av;
 };
-
-// Two transposing 8-byte reads (rows r and r + 1 of each lane's pattern) of one
-// 16-column block, as an 8-element operand.
-__device__ __forceinline__ half8 tr_pair(const _Float16* lo_p, const _Float16* hi_p) {
-  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)lo_p);
-  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)hi_p);
-  const half4 l4 = __builtin_bit_cast(half4, lo), h4 = __builtin_bit_cast(half4, hi);
-  return (half8){l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
-}
 
 // V^T operand of PV step i = 2 mb + kb: channels of block mb of wave w, the 32
 // tokens of K-block kb.
@@ -426,24 +269,6 @@ __device__ __forceinline__ float4v packed_scores(const PageRegs<CB>& t, const ha
   return S;
 }
 
-// Masked page: a token with keep false gets zero (scale, zero) words, so its
-// codes contribute 0 to the scores and the tile (its score is set to -inf).
-template <int CB>
-__device__ __forceinline__ void mask_token(PageRegs<CB>& t, bool keep) {
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) t.sz[m][e] = keep ? t.sz[m][e] : 0u;
-  t.rsz.x = keep ? t.rsz.x : 0u;
-  t.rsz.y = keep ? t.rsz.y : 0u;
-}
-
-// Channel of sub-block j of group g (0..15 content, 16, 17 RoPE) in a
-// [content | rope] row.
-__device__ __forceinline__ int group_channel(int g, int j) {
-  return g < NG_C ? GROUP * g + 8 * j : D_C + GROUP * (g - NG_C) + 8 * j;
-}
-
 // Scores and tile row of a token taken from the BF16 buffers (exact in fp16),
 // for the lanes with use set: one MFMA chain over the 18 groups. The other
 // lanes read a valid row (in bounds), contribute 0 and leave the tile alone.
@@ -492,16 +317,6 @@ __device__ __forceinline__ float4v bf16_page_scores(const PageRegs<16>& t, bool 
       *reinterpret_cast<half8*>(tile + row * TS + GROUP * g + 8 * j) = bf16x8_to_f16x8_rtz(kv);
   }
   return S;
-}
-
-// Sum over the 16 lanes of a row (DPP butterfly: neighbours, pairs, half-row
-// mirror, row mirror).
-__device__ __forceinline__ float row_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
-  return v;
 }
 
 // Page range [it0, it0 + n_it) of workgroup `split` (of n_split) over the
@@ -917,11 +732,17 @@ SplitPlan plan_splits(int B, int H, int max_pages) {
 
 size_t decode_workspace_bytes(int B, int H, int max_pages) {
   const SplitPlan sp = plan_splits(B, H, max_pages);
-  return (size_t)B * sp.n_split * H * (sizeof(float) + D_C * sizeof(_Float16));
+  const size_t narrow = (size_t)B * sp.n_split * H * (sizeof(float) + D_C * sizeof(_Float16));
+  // rows that may be s_q query tokens of 128 heads each (the 128-head path)
+  const size_t wide = H % 128 == 0 ? wide_workspace_bytes(B, H / 128) : 0;
+  return narrow > wide ? narrow : wide;
 }
 
 hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
+  // 128 heads per query token over a packed cache: one dequantization per
+  // page and 64 heads, work split by page weight (decode_wide.hip)
+  if (c_bits != 16 && a.h_per_q == 128) return launch_decode_wide(a, a.ws_lse, c_bits, stream);
   const int n_u = a.B * a.n_split;
   const dim3 grid((n_u + 7) / 8 * 8 * (a.H / 16));
   if (c_bits == 16)

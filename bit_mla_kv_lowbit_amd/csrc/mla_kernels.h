@@ -39,6 +39,7 @@ struct DecodeArgs {
   const uint16_t* local;
   _Float16* ws_o;  // [B, n_split, H, 512] fp16 partial outputs (normalized)
   float* ws_lse;   // [B, n_split, H] fp32 partial log-sum-exp (natural log)
+  int32_t* ws_meta;  // 128-head path: per (sequence, query token) the chunks touching it
   uint16_t* out;  // bf16 [B, H, 512]
   float* lse;     // fp32 [B, H]
   int B, H, n_split, pages_per_split, n_sink, n_local;
@@ -64,5 +65,10 @@ size_t decode_workspace_bytes(int B, int H, int max_pages);
 hipError_t launch_write(const WriteArgs& a, int c_bits, hipStream_t stream);  // c_bits 16: BF16 pages
 hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream);  // c_bits 16: BF16 pages
 hipError_t launch_qdq(const QdqArgs& a, int c_bits, hipStream_t stream);
+
+// 128 heads per query token (packed caches): each page is dequantized once per
+// 64 heads; work split by page weight on the device (decode_wide.hip).
+size_t wide_workspace_bytes(int B, int s_q);
+hipError_t launch_decode_wide(DecodeArgs a, void* workspace, int c_bits, hipStream_t stream);
 
 }  // namespace mla

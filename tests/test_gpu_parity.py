@@ -173,14 +173,16 @@ def test_decode_full_and_short_rows_in_one_batch(c_bits, H):
 
 
 def test_decode_single_range_writes_output_directly():
-    """With enough sequences x head blocks to fill the GPU (64 x 8) and short
-    page tables, each sequence is one page range: the decode writes out / lse
-    itself and no combine runs."""
+    """64 short sequences at H = 128 (1..300 tokens): most of them fall inside
+    one chunk of the length-aware split, whose workgroup writes out / lse
+    itself; the rest are merged from their chunk partials."""
     cfg = _cfg(4)
     lens = [(37 * b) % 300 + 1 for b in range(64)]
     inp = synth.build_cache_inputs(lens, 128, seed=61, device="cpu")
-    # one range per sequence: the workspace holds a single partial per (b, h)
-    assert mla.decode_workspace_bytes(cfg, 64, 128, inp.page_table.shape[1]) == 64 * 128 * 1028
+    # the H = 128 workspace: per-sequence chunk bounds (int2, padded to 256 B)
+    # and (128 chunks + 64 sequences) partial slots of 128 rows (lse + 512 fp16)
+    assert mla.decode_workspace_bytes(cfg, 64, 128, inp.page_table.shape[1]) == \
+        512 + (128 + 64) * 128 * 1028
     print("[case] decode single range B64 H128", flush=True)
     pages, sink, local = gpu_cache(cfg, inp, len(lens))
     out, lse = gpu_decode(cfg, inp, pages, sink, local)
