@@ -54,7 +54,8 @@ def algorithmic_flops(lens, H):
     return 2 * (576 + 512) * H * sum(lens)
 
 
-DECODE_SOURCES = ("bit_mla_kv_lowbit_amd/csrc/decode.hip", "bit_mla_kv_lowbit_amd/csrc/mla_common.h",
+DECODE_SOURCES = ("bit_mla_kv_lowbit_amd/csrc/decode.hip", "bit_mla_kv_lowbit_amd/csrc/decode_wide.hip",
+                  "bit_mla_kv_lowbit_amd/csrc/decode_ops.h", "bit_mla_kv_lowbit_amd/csrc/mla_common.h",
                   "bit_mla_kv_lowbit_amd/csrc/mla_kernels.h")
 
 
@@ -298,9 +299,10 @@ def main():
         f"x{tr['copy_calibration']:.4f} and write x{tr['write_calibration']:.4f} by what the "
         f"counters read for a 512 MiB copy kernel; not measured in this run"
         if tr else "null: no counter summary taken on these kernel sources")
-    roof["kernel"] = ("mla_lowbit_decode: decode_kernel + combine_kernel"
-                      if step is None else
-                      "mla_lowbit_write_decode: write_kernel + decode_kernel + combine_kernel")
+    kernels = ("decode_wide_kernel + combine_wide_kernel" if wl.H == 128
+               else "decode_kernel + combine_kernel")
+    roof["kernel"] = (f"mla_lowbit_decode: {kernels}" if step is None else
+                      f"mla_lowbit_write_decode: write_kernel + {kernels}")
     roof["algorithmic_bytes_per_launch"] = abytes
     roof["algorithmic_flops_per_launch"] = aflops
     roof["hbm_frac"] = round(bw / PEAK_HBM_GBS, 4)
