@@ -559,6 +559,53 @@ def paired_bf16(args, wl, inp, t_lowbit_us, lowbit_cache_bytes, step=None):
             "cache_compression": round(nbytes / lowbit_cache_bytes, 3)}
 
 
+def sweep_cpu_check(inp, out, lse, B, L, H):
+    """CPU leg of one sweep length: the oracle writes the last sequence's L
+    tokens into a compact page table of its own (physical page ids do not enter
+    the result) and decodes all H heads of it, timed; the GPU rows of that
+    sequence are checked against it at the decode tolerance."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    oc = oracle.Cfg(c_bits=4)
+    n_thr = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        n_thr = max(1, min(n_thr, int(os.environ["OMP_NUM_THREADS"])))
+    oracle.set_num_threads(n_thr)
+    u16 = lambda t: t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    b = B - 1
+    n_pages = max(1, -(-L // 64))
+    pt = np.arange(n_pages, dtype=np.int32)[None]
+    lens = np.array([L], np.int32)
+    op = np.zeros((n_pages, oracle.page_bytes(oc)), np.uint8)
+    osink = np.zeros((1, oc.n_sink, 576), np.uint16)
+    olocal = np.zeros((1, oc.n_local, 576), np.uint16)
+    t0 = time.perf_counter()
+    oracle.write(oc, u16(inp.c_kv[b * L:(b + 1) * L]), u16(inp.k_rope[b * L:(b + 1) * L]),
+                 np.zeros(L, np.int32), np.arange(L, dtype=np.int32), lens, pt, op, osink, olocal)
+    t1 = time.perf_counter()
+    ref, rl = oracle.decode(oc, synth.SOFTMAX_SCALE, u16(inp.q_lat[b:b + 1]),
+                            u16(inp.q_rope[b:b + 1]), op, pt, lens, osink, olocal,
+                            sel=[(0, h) for h in range(H)])
+    t2 = time.perf_counter()
+    got = out[b].float().cpu().numpy()
+    gl = lse[b].cpu().numpy()
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    mx = float(np.max(np.abs(got - ref) / np.maximum(1.0, np.abs(ref))))
+    dl = float(np.max(np.abs(gl - rl)))
+    cpu = {"value": round(L / (t2 - t1), 1), "unit": "tokens/s", "cores": n_thr, "kind": "oracle",
+           "sample": f"sequence {b} ({L} cache tokens) x all {H} heads, fp64 plain-loop decode "
+                     f"in {t2 - t1:.1f} s after a {t1 - t0:.1f} s oracle write"}
+    parity = {"rows": H, "rel_l2": rel, "max_abs_rel": mx, "lse_abs": dl,
+              "pass": bool(rel <= 2e-3 and mx <= 1e-2 and dl <= 1e-3)}
+    print(f"[sweep] L{L} oracle check on sequence {b}: rel_l2 {rel:.2e} max {mx:.2e} "
+          f"lse {dl:.2e}", file=sys.stderr, flush=True)
+    return cpu, parity
+
+
 def run_sweep(args, lengths):
     """Context sweep (Figure 5 and Table 9 of the pages): for each length, B
     sequences of H = 16 heads decoded from a C4R4 cache and from a BF16 cache;
@@ -600,6 +647,7 @@ def run_sweep(args, lengths):
         t_low = sum(ev) / len(ev) * 1e3
         low_samples = [v * 1e3 for v in ev]
         del reps, pages, sink, local
+        check = None if args.no_cpu else sweep_cpu_check(inp, out, lse, B, L, H)
         t_bf16, bf16_bytes = time_bf16_decode(args, inp, B, H)
         lens = [L] * B
         table_bytes = inp.page_table.numel() * 4
@@ -614,6 +662,8 @@ def run_sweep(args, lengths):
                 "alloc_c4r4_bytes": low_bytes + table_bytes,
                 "alloc_bf16_bytes": bf16_bytes + table_bytes,
                 "compression": round((bf16_bytes + table_bytes) / (low_bytes + table_bytes), 3)}
+        if check is not None:
+            line["cpu_baseline"], line["parity"] = check
         if args.eager:
             import numpy as np
 

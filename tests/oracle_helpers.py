@@ -51,3 +51,21 @@ def oracle_decode_mq(cfg, inp, pages, sink, local, scale, s_q: int, H: int):
                                  p_end=end)
             out[b, i], lse[b, i] = o, l
     return out, lse
+
+
+def oracle_sequence_rows(cfg, c_kv, k_rope, q_lat_b, q_rope_b, L: int, heads, scale):
+    """Oracle decode of one sequence whose tokens 0..L-1 are c_kv / k_rope (in
+    order), written into a compact page table of its own (the physical page ids
+    do not enter the result). q_lat_b / q_rope_b: [H, d] of that sequence.
+    Returns (out [len(heads), d_c], lse [len(heads)])."""
+    n_pages = max(1, -(-L // cfg.page_size))
+    pt = np.arange(n_pages, dtype=np.int32)[None]
+    lens = np.array([L], np.int32)
+    D = cfg.d_c + cfg.d_r
+    pages = np.zeros((n_pages, oracle.page_bytes(cfg)), np.uint8)
+    sink = np.zeros((1, max(cfg.n_sink, 1), D), np.uint16)
+    local = np.zeros((1, max(cfg.n_local, 1), D), np.uint16)
+    oracle.write(cfg, u16(c_kv), u16(k_rope), np.zeros(L, np.int32),
+                 np.arange(L, dtype=np.int32), lens, pt, pages, sink, local)
+    return oracle.decode(cfg, scale, u16(q_lat_b[None]), u16(q_rope_b[None]), pages, pt, lens,
+                         sink, local, sel=[(0, int(h)) for h in heads])

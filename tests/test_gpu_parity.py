@@ -21,7 +21,7 @@ import bit_mla_kv_lowbit_amd as mla
 import oracle
 import synth
 from tests.gpu_helpers import (DEV, assert_decode_ok, gpu_cache, gpu_decode, ocfg_of, u16)
-from tests.oracle_helpers import oracle_cache, oracle_decode, oracle_decode_mq
+from tests.oracle_helpers import oracle_cache, oracle_decode, oracle_decode_mq, oracle_sequence_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -567,3 +567,30 @@ def test_ranges_longer_than_256_pages():
                                    u16(inp.q_rope), ob, inp.page_table.cpu().numpy(),
                                    inp.seq_lens.cpu().numpy(), sel=rows)
     assert_decode_ok(o16, l16, r16, rl16, rows=rows, label="313-page ranges, bf16")
+
+
+@pytest.mark.parametrize("B,L", [(8, 1048576), (32, 486400)])
+def test_long_context_sweep_sampled(B, L):
+    """The context sweep's launch at its longest contexts (H = 16, one bulk
+    write, the default workspace): B8 at 1M tokens (one round of workgroups,
+    page ranges just past 256 pages) and B32 at 486,400 tokens (one round, ranges
+    of about 475 pages, near the 512-item cap). The first and last sequences,
+    every head, against the oracle."""
+    H = 16
+    cfg = _cfg(4)
+    oc = ocfg_of(cfg)
+    print(f"[case] long-context sweep B{B} H{H} L{L}", flush=True)
+    inp = synth.bulk_cache_inputs(B, L, H, seed=2100 + B, device=DEV)
+    pages, sink, local = mla.allocate_cache(cfg, B, inp.num_pages, DEV)
+    mla.write(cfg, inp.c_kv, inp.k_rope, inp.seq_idx, inp.pos, inp.seq_lens, inp.page_table,
+              pages, sink, local)
+    out, lse = mla.decode(cfg, inp.q_lat, inp.q_rope, pages, inp.page_table, inp.seq_lens, sink,
+                          local, synth.SOFTMAX_SCALE)
+    torch.cuda.synchronize()
+    del pages, sink, local
+    for b in (0, B - 1):
+        ref, ref_lse = oracle_sequence_rows(oc, inp.c_kv[b * L:(b + 1) * L], inp.k_rope[b * L:(b + 1) * L],
+                                            inp.q_lat[b], inp.q_rope[b], L, range(H),
+                                            synth.SOFTMAX_SCALE)
+        assert_decode_ok(out, lse, ref, ref_lse, rows=[(b, h) for h in range(H)],
+                         label=f"sweep B{B} L{L} seq {b}")

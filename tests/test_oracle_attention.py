@@ -320,3 +320,22 @@ def test_multi_query_causal_equals_sdpa(s_q):
             rl = torch.logsumexp(s.masked_fill(~mask[i], float("-inf")), dim=-1)
             np.testing.assert_allclose(out[b, i], ro.numpy(), rtol=1e-12, atol=1e-12)
             np.testing.assert_allclose(lse[b, i], rl.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_compact_page_table_gives_the_same_rows():
+    """A sequence decoded from a compact page table of its own (the long-context
+    GPU tests and the sweep's CPU leg do this) gives the same rows as from the
+    shared, shuffled page table of the whole batch: physical page ids do not
+    enter the result."""
+    from tests.oracle_helpers import oracle_sequence_rows
+    lens = [300, 1000, 777]
+    inp = synth.build_cache_inputs(lens, 4, seed=31)
+    oc = oracle.Cfg(c_bits=4)
+    pages, sink, local = oracle_cache(oc, inp, len(lens))
+    full, full_lse = oracle.decode(oc, synth.SOFTMAX_SCALE, u16(inp.q_lat), u16(inp.q_rope), pages,
+                                   inp.page_table.numpy(), inp.seq_lens.numpy(), sink, local,
+                                   sel=[(1, h) for h in range(4)])
+    m = inp.seq_idx == 1
+    got, got_lse = oracle_sequence_rows(oc, inp.c_kv[m], inp.k_rope[m], inp.q_lat[1], inp.q_rope[1],
+                                        1000, range(4), synth.SOFTMAX_SCALE)
+    assert np.array_equal(full, got) and np.array_equal(full_lse, got_lse)
