@@ -9,7 +9,10 @@
  *
  * Readings of the pages (QuantMLA, newx.sg summary page and thelatestinai.com
  * cards page) where they leave a step open:
- *  Q1 Quantizer: per token and per group of `group` contiguous channels,
+ *  Q1 Quantizer: per token and per group of `group` contiguous channels
+ *     (32 in the workloads; 64 and 128 as variants; a group never spans the
+ *     content / RoPE boundary, and a vector narrower than the group, the
+ *     64-channel RoPE key at group 128, is one group of its own width),
  *     asymmetric min-max round-to-nearest (the RTN baseline row of Table 1 is
  *     the plain quantizer; QuantMLA's learned transforms are fused into the
  *     weights offline per the abstract, so the runtime writer sees
@@ -19,15 +22,18 @@
  *     rint, RNE fp32->fp16. Ties go to the even code.
  *  Q3 A group whose fp16 scale is zero gets all-zero codes.
  *  Q4 Code order (the pages give none; chosen so that one 128-bit load hands
- *     a GPU lane the same 8-channel sub-block of several groups): a vector of
- *     n_g groups of 32 channels at b bits is cut into chunks of u = min(n_g, 16/b)
- *     groups; chunk (ld, j) lies at byte u*b*(4*ld + j) and holds sub-block j
- *     (channels 8j..8j+7 of each group) of groups u*ld .. u*ld+u-1. Inside a chunk,
- *     group u*ld + gi sits in 32-bit little-endian word gi / (4/b), code block
- *     e = gi mod (4/b); channel 8j + 2i + k of the group sits at bit
+ *     a GPU lane the same 8-channel sub-block of several blocks). It is
+ *     defined on blocks of 32 channels, whatever the quantization group: a
+ *     vector of n_g blocks at b bits is cut into chunks of u = min(n_g, 16/b)
+ *     blocks; chunk (ld, j) lies at byte u*b*(4*ld + j) and holds sub-block j
+ *     (channels 8j..8j+7 of each block) of blocks u*ld .. u*ld+u-1. Inside a
+ *     chunk, block u*ld + gi sits in 32-bit little-endian word gi / (4/b),
+ *     code block e = gi mod (4/b); channel 8j + 2i + k of the block sits at bit
  *     16k + b*(4e + i): even channels fill the low half-word, odd ones the high.
+ *     With 32-channel groups a block is a group.
  *  Q5 Page layout: page_size token slots, four token-major regions: content
- *     codes, RoPE codes, content (scale, zero) fp16 pairs, RoPE pairs.
+ *     codes, RoPE codes, content (scale, zero) fp16 pairs (one per content
+ *     group), RoPE pairs (one per RoPE group).
  *  Q6 Protection (sink4/local128 of Figure 5 and Table 9; Figure 8): token p
  *     of a sequence of length L is read from the sink buffer if p < n_sink,
  *     else from the local ring (slot p mod n_local) if p >= L - n_local, else
@@ -69,9 +75,11 @@ int orc_check_cfg(const orc_cfg* c) {
   if (!c) return -1;
   if (c->c_bits != 2 && c->c_bits != 4) return -1;
   if (c->r_bits != 2 && c->r_bits != 4) return -1;
-  if (c->group != 32) return -1; /* the code order works in 8-channel sub-blocks */
-  if (c->d_c <= 0 || c->d_c % c->group != 0) return -1;
-  if (c->d_r <= 0 || c->d_r % c->group != 0) return -1;
+  if (c->group != 32 && c->group != 64 && c->group != 128) return -1;
+  /* the code order works in 32-channel blocks of 8-channel sub-blocks */
+  if (c->d_c <= 0 || c->d_c % 32 != 0 || c->d_c % c->group != 0) return -1;
+  if (c->d_r <= 0 || c->d_r % 32 != 0) return -1;
+  if (c->d_r % (c->group < c->d_r ? c->group : c->d_r) != 0) return -1;
   /* a chunk must hold at least one whole 32-bit word */
   if ((c->d_c / 32) * c->c_bits < 4 && c->c_bits == 2) return -1;
   if ((c->d_r / 32) * c->r_bits < 4 && c->r_bits == 2) return -1;
@@ -190,11 +198,17 @@ void orc_quantize_group(const float* x, int n, int bits, uint16_t* s16, uint16_t
 
 static size_t code_bytes(int d, int bits) { return (size_t)d * (size_t)bits / 8u; }
 
+/* Channels per quantization group of a d-channel vector (reading Q1). */
+static int group_of(const orc_cfg* c, int d) { return c->group < d ? c->group : d; }
+
+/* (scale, zero) bytes per token of a d-channel vector. */
+static size_t sz_bytes(const orc_cfg* c, int d) { return (size_t)(d / group_of(c, d)) * 4u; }
+
 void orc_page_regions(const orc_cfg* c, size_t off[4]) {
   size_t P = (size_t)c->page_size;
   size_t cc = code_bytes(c->d_c, c->c_bits);
   size_t rc = code_bytes(c->d_r, c->r_bits);
-  size_t cs = (size_t)(c->d_c / c->group) * 4u;
+  size_t cs = sz_bytes(c, c->d_c);
   off[0] = 0;
   off[1] = P * cc;
   off[2] = P * (cc + rc);
@@ -204,17 +218,17 @@ void orc_page_regions(const orc_cfg* c, size_t off[4]) {
 size_t orc_page_bytes(const orc_cfg* c) {
   size_t P = (size_t)c->page_size;
   return P * (code_bytes(c->d_c, c->c_bits) + code_bytes(c->d_r, c->r_bits) +
-              (size_t)(c->d_c / c->group) * 4u + (size_t)(c->d_r / c->group) * 4u);
+              sz_bytes(c, c->d_c) + sz_bytes(c, c->d_r));
 }
 
 /* Byte offset of the 32-bit word and bit offset inside it of channel ch of a
- * vector of n_g groups of 32 channels stored at `bits` bits (reading Q4). */
+ * vector of n_g blocks of 32 channels stored at `bits` bits (reading Q4). */
 static void code_position(int n_g, int bits, int ch, int* byte_off, int* bit_off) {
   int g = ch / 32, c = ch % 32;
   int j = c / 8, i = (c % 8) / 2, k = c % 2;
-  int u = n_g < 16 / bits ? n_g : 16 / bits; /* groups per chunk */
+  int u = n_g < 16 / bits ? n_g : 16 / bits; /* blocks per chunk */
   int ld = g / u, gi = g % u;
-  int per_word = 4 / bits; /* groups sharing one word */
+  int per_word = 4 / bits; /* blocks sharing one word */
   int w = gi / per_word, e = gi % per_word;
   *byte_off = u * bits * (4 * ld + j) + 4 * w;
   *bit_off = 16 * k + bits * (4 * e + i);
@@ -253,7 +267,7 @@ static void pack_vector(const uint16_t* in, int d, int bits, int group, uint8_t*
   for (int w = 0; w < d * bits / 32; ++w) put_u32(code_dst + 4 * w, 0u);
   for (int ch = 0; ch < d; ++ch) {
     int byte_off, bit_off;
-    code_position(d / group, bits, ch, &byte_off, &bit_off);
+    code_position(d / 32, bits, ch, &byte_off, &bit_off);
     uint32_t word = get_u32(code_dst + byte_off);
     word |= (uint32_t)q[ch] << bit_off;
     put_u32(code_dst + byte_off, word);
@@ -278,7 +292,7 @@ int orc_write(const orc_cfg* c, int n, const uint16_t* c_kv, const uint16_t* k_r
   orc_page_regions(c, off);
   const size_t pb = orc_page_bytes(c);
   const size_t cc = code_bytes(c->d_c, c->c_bits), rc = code_bytes(c->d_r, c->r_bits);
-  const size_t cs = (size_t)(c->d_c / c->group) * 4u, rs = (size_t)(c->d_r / c->group) * 4u;
+  const size_t cs = sz_bytes(c, c->d_c), rs = sz_bytes(c, c->d_r);
   const int D = c->d_c + c->d_r;
   /* validate every index first, then write (tokens are independent: each
    * (sequence, position) appears once, so no two tokens share a slot) */
@@ -299,9 +313,9 @@ int orc_write(const orc_cfg* c, int n, const uint16_t* c_kv, const uint16_t* k_r
     uint8_t* base = pages + (size_t)page * pb;
     const uint16_t* xc = c_kv + (size_t)t * c->d_c;
     const uint16_t* xr = k_rope + (size_t)t * c->d_r;
-    pack_vector(xc, c->d_c, c->c_bits, c->group, base + off[0] + slot * cc,
+    pack_vector(xc, c->d_c, c->c_bits, group_of(c, c->d_c), base + off[0] + slot * cc,
                 base + off[2] + slot * cs);
-    pack_vector(xr, c->d_r, c->r_bits, c->group, base + off[1] + slot * rc,
+    pack_vector(xr, c->d_r, c->r_bits, group_of(c, c->d_r), base + off[1] + slot * rc,
                 base + off[3] + slot * rs);
     uint16_t* dst = NULL;
     int src = orc_token_source(c, p, L);
@@ -324,7 +338,7 @@ static void unpack_vector(const uint8_t* code_src, const uint8_t* sz_src, int d,
   uint32_t mask = (1u << bits) - 1u;
   for (int i = 0; i < d; ++i) {
     int byte_off, bit_off;
-    code_position(d / group, bits, i, &byte_off, &bit_off);
+    code_position(d / 32, bits, i, &byte_off, &bit_off);
     uint32_t q = (get_u32(code_src + byte_off) >> bit_off) & mask;
     int g = i / group;
     double s = orc_f16_to_f64(get_u16(sz_src + 4 * g));
@@ -351,14 +365,14 @@ int orc_token_values(const orc_cfg* c, int b, int p, const uint8_t* pages,
   orc_page_regions(c, off);
   const size_t pb = orc_page_bytes(c);
   const size_t cc = code_bytes(c->d_c, c->c_bits), rc = code_bytes(c->d_r, c->r_bits);
-  const size_t cs = (size_t)(c->d_c / c->group) * 4u, rs = (size_t)(c->d_r / c->group) * 4u;
+  const size_t cs = sz_bytes(c, c->d_c), rs = sz_bytes(c, c->d_r);
   int64_t page = page_table[(size_t)b * max_pages + p / c->page_size];
   int slot = p % c->page_size;
   const uint8_t* base = pages + (size_t)page * pb;
   unpack_vector(base + off[0] + slot * cc, base + off[2] + slot * cs, c->d_c, c->c_bits,
-                c->group, kc);
+                group_of(c, c->d_c), kc);
   unpack_vector(base + off[1] + slot * rc, base + off[3] + slot * rs, c->d_r, c->r_bits,
-                c->group, kr);
+                group_of(c, c->d_r), kr);
   return 0;
 }
 
@@ -575,9 +589,9 @@ int orc_qdq(const orc_cfg* c, int n, const uint16_t* c_kv, const uint16_t* k_rop
             uint16_t* out_c, uint16_t* out_r) {
   if (orc_check_cfg(c)) return -1;
   for (int t = 0; t < n; ++t) {
-    qdq_vector(c_kv + (size_t)t * c->d_c, c->d_c, c->c_bits, c->group,
+    qdq_vector(c_kv + (size_t)t * c->d_c, c->d_c, c->c_bits, group_of(c, c->d_c),
                out_c + (size_t)t * c->d_c);
-    qdq_vector(k_rope + (size_t)t * c->d_r, c->d_r, c->r_bits, c->group,
+    qdq_vector(k_rope + (size_t)t * c->d_r, c->d_r, c->r_bits, group_of(c, c->d_r),
                out_r + (size_t)t * c->d_r);
   }
   return 0;

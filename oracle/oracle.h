@@ -38,7 +38,7 @@ typedef struct {
   int32_t d_r;       /* decoupled RoPE key width (64) */
   int32_t c_bits;    /* content code width: 4 or 2 */
   int32_t r_bits;    /* RoPE code width: 4 or 2 */
-  int32_t group;     /* channels per quantization group (32) */
+  int32_t group;     /* channels per quantization group: 32, 64 or 128 */
   int32_t page_size; /* token slots per page (64) */
   int32_t n_sink;    /* leading protected tokens (4) */
   int32_t n_local;   /* trailing protected tokens (128) */

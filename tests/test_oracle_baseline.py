@@ -103,26 +103,28 @@ def _bf16_of(x: np.ndarray) -> np.ndarray:
     return (u >> 16).astype(np.uint16)
 
 
-@pytest.mark.parametrize("c_bits", [4, 2])
-def test_qdq_representable_groups_are_unchanged(c_bits):
-    cfg = oracle.Cfg(c_bits=c_bits)
+@pytest.mark.parametrize("c_bits,r_bits,group", [(4, 4, 32), (2, 4, 32), (2, 2, 64),
+                                                 (4, 2, 128)])
+def test_qdq_representable_groups_are_unchanged(c_bits, r_bits, group):
+    cfg = oracle.Cfg(c_bits=c_bits, r_bits=r_bits, group=group)
     rng = np.random.default_rng(7)
     n = 6
 
     def rows(d, bits):
         qmax = (1 << bits) - 1
+        w = min(group, d)
         out = np.zeros((n, d), np.float32)
         for t in range(n):
-            for g in range(d // 32):
+            for g in range(d // w):
                 s = 2.0 ** int(rng.integers(-6, 2))
                 z = int(rng.integers(-100, 100)) * s
-                k = rng.integers(0, qmax + 1, 32)
+                k = rng.integers(0, qmax + 1, w)
                 k[0], k[1] = 0, qmax
                 rng.shuffle(k)
-                out[t, 32 * g:32 * g + 32] = z + k * s
+                out[t, w * g:w * g + w] = z + k * s
         return out
 
-    xc, xr = rows(cfg.d_c, c_bits), rows(cfg.d_r, 4)
+    xc, xr = rows(cfg.d_c, c_bits), rows(cfg.d_r, r_bits)
     oc, orr = oracle.qdq(cfg, _bf16_of(xc), _bf16_of(xr))
     np.testing.assert_array_equal(oc, _bf16_of(xc))
     np.testing.assert_array_equal(orr, _bf16_of(xr))
@@ -146,11 +148,12 @@ def test_qdq_error_bound(c_bits):
     assert np.all(err <= bound + 1e-12)
 
 
-@pytest.mark.parametrize("c_bits", [4, 2])
-def test_qdq_matches_dequantized_packed_copy(c_bits):
+@pytest.mark.parametrize("c_bits,r_bits,group", [(4, 4, 32), (2, 4, 32), (4, 2, 64),
+                                                 (2, 2, 128)])
+def test_qdq_matches_dequantized_packed_copy(c_bits, r_bits, group):
     """qdq(x) equals the attention-side values of x's packed copy (read back
     through the page layout), rounded to fp32 and then to bf16."""
-    cfg = oracle.Cfg(c_bits=c_bits, n_sink=0, n_local=0)
+    cfg = oracle.Cfg(c_bits=c_bits, r_bits=r_bits, group=group, n_sink=0, n_local=0)
     L = 150
     inp = synth.build_cache_inputs([L], 1, seed=35, device="cpu")
     pages, sink, local = oracle_cache(cfg, inp, 1)

@@ -21,15 +21,16 @@ def _levels(s16, z16, bits):
     return np.arange(1 << bits) * s + z, s
 
 
+@pytest.mark.parametrize("n", [32, 64, 128])
 @pytest.mark.parametrize("bits", [2, 4])
 @pytest.mark.parametrize("kind", ["normal", "outlier", "tiny", "shifted"])
-def test_codes_are_nearest_level(bits, kind):
-    rng = np.random.default_rng(10 + bits)
+def test_codes_are_nearest_level(bits, kind, n):
+    rng = np.random.default_rng(10 + bits + n)
     n_bad = 0
-    for trial in range(400):
-        x = rng.standard_normal(32)
+    for trial in range(400 * 32 // n):
+        x = rng.standard_normal(n)
         if kind == "outlier":
-            x[rng.integers(0, 32)] *= 10.0
+            x[rng.integers(0, n)] *= 10.0
         elif kind == "tiny":
             x *= 1e-3
         elif kind == "shifted":
@@ -40,7 +41,7 @@ def test_codes_are_nearest_level(bits, kind):
         assert s > 0
         d = np.abs(x.astype(np.float64)[:, None] - lv[None, :])
         best = np.argmin(d, axis=1)
-        for i in range(32):
+        for i in range(n):
             if q[i] == best[i]:
                 continue
             # only a near-tie (decided by fp32 rounding of (x - z) / s) may differ
@@ -66,18 +67,19 @@ def test_reconstruction_error_bound(bits):
         assert np.all(np.abs(x - xh) <= s / 2 + slack + 1e-12)
 
 
+@pytest.mark.parametrize("n", [32, 64, 128])
 @pytest.mark.parametrize("bits", [2, 4])
-def test_representable_round_trip(bits):
-    rng = np.random.default_rng(4)
+def test_representable_round_trip(bits, n):
+    rng = np.random.default_rng(4 + n)
     qmax = (1 << bits) - 1
     for _ in range(200):
         e = int(rng.integers(-8, 3))
         s = 2.0 ** e
         m = int(rng.integers(-200, 200))
         z = m * s
-        k = rng.integers(0, qmax + 1, 32)
-        k[rng.integers(0, 32)] = 0
-        k[rng.integers(0, 32)] = qmax
+        k = rng.integers(0, qmax + 1, n)
+        k[rng.integers(0, n)] = 0
+        k[rng.integers(0, n)] = qmax
         if k.min() != 0 or k.max() != qmax:
             k[0], k[1] = 0, qmax
         x = (z + k * s).astype(np.float32)
@@ -159,6 +161,53 @@ def test_golden_packing_c2():
     off = oracle.page_regions(cfg)
     assert bytes(page[off[0]:off[0] + 16]) == g["content_codes"]
     assert bytes(page[off[2]:off[2] + 8]) == g["content_sz"]
+
+
+def test_golden_packing_c2r2_group64():
+    """2-bit RoPE codes and a 64-channel quantization group (tests/golden)."""
+    cfg = oracle.Cfg(d_c=64, d_r=64, c_bits=2, r_bits=2, group=64, page_size=1, n_sink=0,
+                     n_local=0)
+    cvals = [(c % 4) * 0.25 for c in range(32)] + [(c // 8) * 0.5 for c in range(32)]
+    rvals = [float(c % 4) for c in range(32)] + [float(3 - c % 4) for c in range(32)]
+    page = _write_one(cfg, cvals, rvals)
+    g = _read_golden("pack_c2r2_g64_tiny.txt")
+    off = oracle.page_regions(cfg)
+    assert off == [0, 16, 32, 36] and oracle.page_bytes(cfg) == 40
+    assert bytes(page[0:16]) == g["content_codes"]
+    assert bytes(page[16:32]) == g["rope_codes"]
+    assert bytes(page[32:36]) == g["content_sz"]
+    assert bytes(page[36:40]) == g["rope_sz"]
+
+
+def test_golden_packing_c4r4_group128():
+    """A 128-channel group over the content and a RoPE vector narrower than
+    the group, which forms one group of its own width (tests/golden)."""
+    cfg = oracle.Cfg(d_c=128, d_r=64, c_bits=4, r_bits=4, group=128, page_size=1, n_sink=0,
+                     n_local=0)
+    cvals = [float(c % 4 + 4 * (c // 32)) for c in range(128)]
+    rvals = [(c % 4) * 0.5 for c in range(32)] + [(12 + c % 4) * 0.5 for c in range(32)]
+    page = _write_one(cfg, cvals, rvals)
+    g = _read_golden("pack_c4r4_g128_tiny.txt")
+    off = oracle.page_regions(cfg)
+    assert off == [0, 64, 96, 100] and oracle.page_bytes(cfg) == 104
+    assert bytes(page[0:64]) == g["content_codes"]
+    assert bytes(page[64:96]) == g["rope_codes"]
+    assert bytes(page[96:100]) == g["content_sz"]
+    assert bytes(page[100:104]) == g["rope_sz"]
+
+
+@pytest.mark.parametrize("c_bits,r_bits,group,per_token", [
+    (4, 4, 64, 256 + 32 + 8 * 4 + 1 * 4), (4, 4, 128, 256 + 32 + 4 * 4 + 1 * 4),
+    (4, 2, 32, 256 + 16 + 16 * 4 + 2 * 4), (2, 2, 32, 128 + 16 + 16 * 4 + 2 * 4),
+    (2, 2, 128, 128 + 16 + 4 * 4 + 1 * 4), (2, 4, 64, 128 + 32 + 8 * 4 + 1 * 4)])
+def test_page_sizes_of_the_variant_layouts(c_bits, r_bits, group, per_token):
+    """Code bytes d * bits / 8 plus one 4-byte (scale, zero) pair per group (the
+    64-channel RoPE key is one group when the group is 128), per token."""
+    cfg = oracle.Cfg(c_bits=c_bits, r_bits=r_bits, group=group)
+    assert oracle.page_bytes(cfg) == 64 * per_token
+    cc, rc = 512 * c_bits // 8, 64 * r_bits // 8
+    assert oracle.page_regions(cfg) == [0, 64 * cc, 64 * (cc + rc),
+                                        64 * (cc + rc + 4 * (512 // group))]
 
 
 def test_page_sizes_of_the_workload_layouts():
