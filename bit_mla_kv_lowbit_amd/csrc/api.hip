@@ -16,12 +16,24 @@ namespace {
 
 int check_cfg(const mla_lowbit_config* c) {
   if (!c) return MLA_LOWBIT_EINVAL;
-  if (c->d_c != D_C || c->d_r != D_R || c->group != GROUP || c->page_size != PAGE)
+  if (c->d_c != D_C || c->d_r != D_R || c->page_size != PAGE) return MLA_LOWBIT_EUNSUPPORTED;
+  if (c->group != 32 && c->group != 64 && c->group != 128) return MLA_LOWBIT_EUNSUPPORTED;
+  if ((c->c_bits != 4 && c->c_bits != 2) || (c->r_bits != 4 && c->r_bits != 2))
     return MLA_LOWBIT_EUNSUPPORTED;
-  if ((c->c_bits != 4 && c->c_bits != 2) || c->r_bits != 4) return MLA_LOWBIT_EUNSUPPORTED;
   if (c->n_sink < 0 || c->n_sink > 64 || c->n_local < 0 || c->n_local > 256)
     return MLA_LOWBIT_EUNSUPPORTED;
   return MLA_LOWBIT_OK;
+}
+
+// Format code of a checked configuration (mla_common.h).
+int fmt_of(const mla_lowbit_config* c) { return fmt_code(c->c_bits, c->r_bits, c->group); }
+
+size_t page_bytes_of(int fmt) {
+  size_t n = 0;
+#define MLA_PAGE_BYTES(F) n = (size_t)PageGeom<F>::BYTES
+  MLA_FOR_PACKED_FMT(fmt, MLA_PAGE_BYTES)
+#undef MLA_PAGE_BYTES
+  return n;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -147,7 +159,7 @@ int mla_lowbit_check_config(const mla_lowbit_config* cfg) { return check_cfg(cfg
 
 size_t mla_lowbit_page_bytes(const mla_lowbit_config* cfg) {
   if (check_cfg(cfg)) return 0;
-  return cfg->c_bits == 4 ? (size_t)PageGeom<4>::BYTES : (size_t)PageGeom<2>::BYTES;
+  return page_bytes_of(fmt_of(cfg));
 }
 
 size_t mla_lowbit_decode_workspace_bytes(const mla_lowbit_config* cfg, int B, int H,
@@ -179,7 +191,7 @@ int mla_lowbit_write(const mla_lowbit_config* cfg, int n_tokens, const void* c_k
   a.local = static_cast<uint16_t*>(local);
   a.n_sink = cfg->n_sink;
   a.n_local = cfg->n_local;
-  return launch_write(a, cfg->c_bits, static_cast<hipStream_t>(stream)) == hipSuccess
+  return launch_write(a, fmt_of(cfg), static_cast<hipStream_t>(stream)) == hipSuccess
              ? MLA_LOWBIT_OK
              : MLA_LOWBIT_ELAUNCH;
 }
@@ -194,7 +206,7 @@ int mla_lowbit_decode(const mla_lowbit_config* cfg, int B, int H, float softmax_
   if (rc || B == 0) return rc;
   DecodeArgs a = make_decode_args(cfg, B, H, softmax_scale, q_lat, q_rope, pages, page_table,
                                   max_pages, seq_lens, sink, local, out, lse, workspace);
-  return launch_decode(a, cfg->c_bits, static_cast<hipStream_t>(stream)) == hipSuccess
+  return launch_decode(a, fmt_of(cfg), static_cast<hipStream_t>(stream)) == hipSuccess
              ? MLA_LOWBIT_OK
              : MLA_LOWBIT_ELAUNCH;
 }
@@ -221,7 +233,7 @@ int mla_lowbit_decode_noalloc(const mla_lowbit_config* cfg, int B, int H, float 
   if (ws == nullptr) return MLA_LOWBIT_ELAUNCH;
   DecodeArgs a = make_decode_args(cfg, B, H, softmax_scale, q_lat, q_rope, pages, page_table,
                                   max_pages, seq_lens, sink, local, out, lse, ws);
-  return launch_decode(a, cfg->c_bits, static_cast<hipStream_t>(stream)) == hipSuccess
+  return launch_decode(a, fmt_of(cfg), static_cast<hipStream_t>(stream)) == hipSuccess
              ? MLA_LOWBIT_OK
              : MLA_LOWBIT_ELAUNCH;
 }
@@ -240,7 +252,7 @@ int mla_lowbit_decode_mq(const mla_lowbit_config* cfg, int B, int s_q, int H,
                                   max_pages, seq_lens, sink, local, out, lse, workspace);
   a.s_q = s_q;
   a.h_per_q = H;
-  return launch_decode(a, cfg->c_bits, static_cast<hipStream_t>(stream)) == hipSuccess
+  return launch_decode(a, fmt_of(cfg), static_cast<hipStream_t>(stream)) == hipSuccess
              ? MLA_LOWBIT_OK
              : MLA_LOWBIT_ELAUNCH;
 }
@@ -273,10 +285,10 @@ int mla_lowbit_write_decode(const mla_lowbit_config* cfg, int B, int H, float so
   w.n_sink = cfg->n_sink;
   w.n_local = cfg->n_local;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_write(w, cfg->c_bits, s) != hipSuccess) return MLA_LOWBIT_ELAUNCH;
+  if (launch_write(w, fmt_of(cfg), s) != hipSuccess) return MLA_LOWBIT_ELAUNCH;
   DecodeArgs a = make_decode_args(cfg, B, H, softmax_scale, q_lat, q_rope, pages, page_table,
                                   max_pages, seq_lens, sink, local, out, lse, workspace);
-  return launch_decode(a, cfg->c_bits, s) == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ELAUNCH;
+  return launch_decode(a, fmt_of(cfg), s) == hipSuccess ? MLA_LOWBIT_OK : MLA_LOWBIT_ELAUNCH;
 }
 
 int mla_lowbit_qdq(const mla_lowbit_config* cfg, int n_tokens, const void* c_kv,
@@ -293,7 +305,7 @@ int mla_lowbit_qdq(const mla_lowbit_config* cfg, int n_tokens, const void* c_kv,
   a.k_rope = static_cast<const uint16_t*>(k_rope);
   a.out_c = static_cast<uint16_t*>(out_c);
   a.out_r = static_cast<uint16_t*>(out_r);
-  return launch_qdq(a, cfg->c_bits, static_cast<hipStream_t>(stream)) == hipSuccess
+  return launch_qdq(a, fmt_of(cfg), static_cast<hipStream_t>(stream)) == hipSuccess
              ? MLA_LOWBIT_OK
              : MLA_LOWBIT_ELAUNCH;
 }

@@ -39,7 +39,7 @@
 // The same kernel serves two related calls. With s_q query tokens per
 // sequence (multi-token prediction, GQLA card) the rows of query token i form
 // their own head blocks and attend to the first L - (s_q - 1 - i) tokens. With
-// CB = 16 it decodes the paired BF16 cache the pages normalize their latency
+// F = 16 it decodes the paired BF16 cache the pages normalize their latency
 // to (Figure 5(b), Table 9): BF16 rows instead of codes, bf16 MFMA for the
 // scores, the same tile, softmax, PV and combine.
 #include "mla_common.h"
@@ -232,8 +232,8 @@ __device__ __forceinline__ void pv_begin(PvCtx& c, AttnState& st, const _Float16
 
 // Scores of the lane's token (S[i]: head 4j + i) over its 18 groups, plus the
 // content tile row of the token.
-template <int CB>
-__device__ __forceinline__ float4v packed_scores(const PageRegs<CB>& t, const half8 (&qA)[18],
+template <int F>
+__device__ __forceinline__ float4v packed_scores(const PageRegs<F>& t, const half8 (&qA)[18],
                                                  const half8& qz1, const half8& qz2,
                                                  _Float16* tile, int row, int j) {
   // z operands (K slot 8j + i): zb1 holds the z of content groups 0..7 in lanes
@@ -256,8 +256,8 @@ __device__ __forceinline__ float4v packed_scores(const PageRegs<CB>& t, const ha
   float sp = 0.f;
 #pragma unroll
   for (int g = 0; g < NG_C + NG_R; ++g) {
-    const half8 c = g < NG_C ? content_codes<CB>(t, g) : codes4(t.r[g - NG_C]);
-    const uint32_t sz = g < NG_C ? content_sz<CB>(t, g) : t.rsz[g - NG_C];
+    const half8 c = g < NG_C ? content_codes<F>(t, g) : rope_codes<F>(t, g - NG_C);
+    const uint32_t sz = g < NG_C ? content_sz<F>(t, g) : t.rsz[g - NG_C];
     const float4v D = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[g], c, zero4, 0, 0, 0);
     if (g > 0) S += sp * Dp;
     if (g < NG_C)
@@ -356,7 +356,7 @@ __device__ __forceinline__ PageRange page_range(int L, int n_s, int lo_start, in
 // buffers in their own slots). Workgroup `split` takes a contiguous range of
 // the pages (an even share of their cost), and writes one partial (O / l,
 // lse) that combine_kernel merges.
-template <int CB>
+template <int F>
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 tile[TILE];
   __shared__ __attribute__((aligned(16))) _Float16 pbuf[PAGE * PS];
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   // physical pages of the first 256 items (a longer range, where the split
   // plan makes one, reads the rest from the page table with scalar loads)
   __shared__ int pids[256];
-  __shared__ __attribute__((aligned(16))) half8 q_lds[CB == 16 ? Q_LDS * 64 : 1];
+  __shared__ __attribute__((aligned(16))) half8 q_lds[F == 16 ? Q_LDS * 64 : 1];
 
   // All scalar arguments are read up front (one round trip, not one per first
   // use: the length, the page table and the first page already form a chain
@@ -456,15 +456,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   // item repeat it; with no item the descriptor has an empty range (loads
   // return 0, touch nothing), so the loads stay unconditional and the wait
   // counts static.
-  const LaneOffsets<CB> lo(row, j);
-  PageRegs<CB> regs;
-  load_page<CB>(regs, page_rsrc<CB>(a.pages, pid0, n_pk > 0), lo);
+  const LaneOffsets<F> lo(row, j);
+  PageRegs<F> regs;
+  load_page<F>(regs, page_rsrc<F>(a.pages, pid0, n_pk > 0), lo);
 #pragma unroll
   for (int i = 0; i < (NCH + 255) / 256; ++i) {
     const int c = tid + 256 * i, hh = c / (D_ALL / 8), k = c % (D_ALL / 8);
     if (c < NCH)
       *reinterpret_cast<half8*>(tile + hh * QS + 8 * k) =
-          CB == 16 ? __builtin_bit_cast(half8, qv[i]) : bf16x8_to_f16x8(qv[i]);
+          F == 16 ? __builtin_bit_cast(half8, qv[i]) : bf16x8_to_f16x8(qv[i]);
   }
   __syncthreads();  // Q staged
 
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < NG_C + NG_R; ++g)
       qA[g] = *reinterpret_cast<const half8*>(tile + t16 * QS + group_channel(g, j));
-    if constexpr (CB == 16) {
+    if constexpr (F == 16) {
       if (w == 0) {
 #pragma unroll
         for (int g = Q_REG; g < NG_C + NG_R; ++g) q_lds[64 * (g - Q_REG) + lane] = qA[g];
@@ -512,21 +512,21 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   if (tid < n_pk) pids[tid] = pid_mine;
   __syncthreads();  // page ids in LDS; Q read out of the tile before it is overwritten
 
-  auto score_item = [&](const PageRegs<CB>& cur, int k) {
+  auto score_item = [&](const PageRegs<F>& cur, int k) {
     const int p0 = (it0 + k) * PAGE;
     const bool mixed = p0 < n_s || p0 + PAGE > mix_from;  // not every token packed
     const int p = p0 + row;
     const bool valid = p < Lq;
     const bool prot = valid && (p < n_s || p >= lo_start);
-    if constexpr (CB == 16) {
+    if constexpr (F == 16) {
       // BF16 baseline: no protected buffers; a partial last page masks its tail
       float4v S = bf16_page_scores(cur, !mixed || valid, qA, q_lds + lane, tile, row, j);
       if (!valid) S = (float4v){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       return S;
     } else {
-      PageRegs<CB> t = cur;
-      if (mixed) mask_token<CB>(t, valid && !prot);
-      float4v S = packed_scores<CB>(t, qA, qz1, qz2, tile, row, j);
+      PageRegs<F> t = cur;
+      if (mixed) mask_token<F>(t, valid && !prot);
+      float4v S = packed_scores<F>(t, qA, qz1, qz2, tile, row, j);
       if (mixed) {
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);  // pages with BF16 rows are the slow ones
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       // barrier do not wait behind a long run of VALU work.
       __builtin_amdgcn_s_setprio(2);
       softmax_tokens(st, S, pl, sl2, w, lane, row, j, t16);
-      load_page<CB>(regs, page_rsrc<CB>(a.pages, n_pk > 0 ? __builtin_amdgcn_readfirstlane(pid_next) : 0,
+      load_page<F>(regs, page_rsrc<F>(a.pages, n_pk > 0 ? __builtin_amdgcn_readfirstlane(pid_next) : 0,
                                         n_pk > 0), lo);
       __syncthreads();
       PvCtx pv;
@@ -738,19 +738,20 @@ size_t decode_workspace_bytes(int B, int H, int max_pages) {
   return narrow > wide ? narrow : wide;
 }
 
-hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream) {
+hipError_t launch_decode(DecodeArgs a, int fmt, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
   // 128 heads per query token over a packed cache: one dequantization per
   // page and 64 heads, work split by page weight (decode_wide.hip)
-  if (c_bits != 16 && a.h_per_q == 128) return launch_decode_wide(a, a.ws_lse, c_bits, stream);
+  if (fmt != 16 && a.h_per_q == 128) return launch_decode_wide(a, a.ws_lse, fmt, stream);
   const int n_u = a.B * a.n_split;
   const dim3 grid((n_u + 7) / 8 * 8 * (a.H / 16));
-  if (c_bits == 16)
+  if (fmt == 16) {
     decode_kernel<16><<<grid, dim3(256), 0, stream>>>(a);
-  else if (c_bits == 4)
-    decode_kernel<4><<<grid, dim3(256), 0, stream>>>(a);
-  else
-    decode_kernel<2><<<grid, dim3(256), 0, stream>>>(a);
+  } else {
+#define MLA_LAUNCH_NARROW(F) decode_kernel<F><<<grid, dim3(256), 0, stream>>>(a)
+    MLA_FOR_PACKED_FMT(fmt, MLA_LAUNCH_NARROW)
+#undef MLA_LAUNCH_NARROW
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;  // one range: output written directly
   // SL split lanes with U ranges each per round of loads (U covers a lane's

@@ -25,12 +25,12 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
   return r;
 }
 
-template <int CB>
+template <int F>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* pages, int pid,
                                                             bool any = true) {
   return __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(pages + (int64_t)pid * PageGeom<CB>::BYTES), (short)0,
-      any ? PageGeom<CB>::BYTES : 0, 0x00020000);
+      (void*)(pages + (int64_t)pid * PageGeom<F>::BYTES), (short)0,
+      any ? PageGeom<F>::BYTES : 0, 0x00020000);
 }
 
 // Exact codes of channels 8j..8j+7 (pairs (0,1) (2,3) (4,5) (6,7)) of one group
@@ -102,14 +102,14 @@ __device__ __forceinline__ float row_sum(float v) {
 }
 
 // Raw data one lane loads for one page: sub-block j of its token in each of the
-// 16 content groups and the 2 RoPE groups, and all (scale, zero) words of its
-// token.
-template <int CB>
+// 16 content blocks and the 2 RoPE blocks, and all (scale, zero) words of its
+// token, one per 32-channel block (a group of 2 or 4 blocks repeats its word).
+template <int F>
 struct PageRegs {
-  u32x4 c[CB == 4 ? 4 : 2];  // content code chunks
-  u32x4 sz[4];               // content (s, z) words of groups 0..15
-  u32x2 r;                   // RoPE code words (groups 0, 1)
-  u32x2 rsz;                 // RoPE (s, z) words
+  u32x4 c[fmt_cb(F) == 4 ? 4 : 2];  // content code chunks
+  u32x4 sz[4];                      // content (s, z) words of blocks 0..15
+  u32x2 r;                          // RoPE code words (4-bit: blocks 0, 1; 2-bit: .x)
+  u32x2 rsz;                        // RoPE (s, z) words of blocks 0, 1
 };
 
 // BF16 baseline page: sub-block j of each of the token's 18 groups, raw bf16.
@@ -121,15 +121,16 @@ struct PageRegs<16> {
 // Byte offsets, inside a page, of what one lane (slot, sub-block j) loads,
 // relative to the start of each region (the region starts go in the scalar
 // offset of the buffer loads). The content code chunk m (16 bytes at + 64 m)
-// holds sub-block j of groups 4m .. 4m + 3 (INT4) or 8m .. 8m + 7 (INT2).
-template <int CB>
+// holds sub-block j of blocks 4m .. 4m + 3 (INT4) or 8m .. 8m + 7 (INT2); the
+// RoPE chunk j holds sub-block j of both RoPE blocks (8 bytes at 4 bits, 4 at 2).
+template <int F>
 struct LaneOffsets {
   uint32_t c, s, r, rs;
   __device__ LaneOffsets(int slot, int j) {
-    using G = PageGeom<CB>;
+    using G = PageGeom<F>;
     c = slot * G::CC + 16 * j;
     s = slot * G::CS;
-    r = slot * G::RC + 8 * j;
+    r = slot * G::RC + (G::RB == 4 ? 8 : 4) * j;
     rs = slot * G::RS;
   }
 };
@@ -144,41 +145,69 @@ struct LaneOffsets<16> {
   __device__ LaneOffsets(int slot, int j) : c(slot * PageGeom<16>::ROW + 16 * j) {}
 };
 
-template <int CB>
-__device__ __forceinline__ void load_page(PageRegs<CB>& t, __amdgpu_buffer_rsrc_t rs,
-                                          const LaneOffsets<CB>& o) {
-  if constexpr (CB == 16) {
+template <int F>
+__device__ __forceinline__ void load_page(PageRegs<F>& t, __amdgpu_buffer_rsrc_t rs,
+                                          const LaneOffsets<F>& o) {
+  if constexpr (F == 16) {
 #pragma unroll
     for (int g = 0; g < NG_C + NG_R; ++g)
       t.k[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.c, 64 * g, 0));
   } else {
-  using G = PageGeom<CB>;
+    using G = PageGeom<F>;
 #pragma unroll
-  for (int m = 0; m < (CB == 4 ? 4 : 2); ++m)
-    t.c[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.c, G::OFF_CC + 64 * m, 0));
+    for (int m = 0; m < (G::CB == 4 ? 4 : 2); ++m)
+      t.c[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.c, G::OFF_CC + 64 * m, 0));
+    if constexpr (G::GM == 1) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    t.sz[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.s, G::OFF_CS + 16 * m, 0));
-  t.r = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.r, G::OFF_RC, 0));
-  t.rsz = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.rs, G::OFF_RS, 0));
+      for (int m = 0; m < 4; ++m)
+        t.sz[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.s, G::OFF_CS + 16 * m, 0));
+    } else if constexpr (G::GM == 2) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.s, G::OFF_CS + 16 * m, 0));
+        t.sz[2 * m] = (u32x4){w.x, w.x, w.y, w.y};
+        t.sz[2 * m + 1] = (u32x4){w.z, w.z, w.w, w.w};
+      }
+    } else {
+      const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.s, G::OFF_CS, 0));
+#pragma unroll
+      for (int m = 0; m < 4; ++m) t.sz[m] = (u32x4){w[m], w[m], w[m], w[m]};
+    }
+    if constexpr (G::RB == 4) {
+      t.r = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.r, G::OFF_RC, 0));
+    } else {
+      t.r = (u32x2){__builtin_amdgcn_raw_buffer_load_b32(rs, o.r, G::OFF_RC, 0), 0u};
+    }
+    if constexpr (G::GMR == 1) {
+      t.rsz = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.rs, G::OFF_RS, 0));
+    } else {
+      const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rs, o.rs, G::OFF_RS, 0);
+      t.rsz = (u32x2){w, w};
+    }
   }
 }
 
-// Codes and (s, z) word of content group g (0..15).
-template <int CB>
-__device__ __forceinline__ half8 content_codes(const PageRegs<CB>& t, int g) {
-  if (CB == 4) return codes4(t.c[g >> 2][g & 3]);
+// Codes and (s, z) word of content block g (0..15).
+template <int F>
+__device__ __forceinline__ half8 content_codes(const PageRegs<F>& t, int g) {
+  if (fmt_cb(F) == 4) return codes4(t.c[g >> 2][g & 3]);
   return codes2(t.c[g >> 3][(g & 7) >> 1], g & 1);
 }
-template <int CB>
-__device__ __forceinline__ uint32_t content_sz(const PageRegs<CB>& t, int g) {
+template <int F>
+__device__ __forceinline__ uint32_t content_sz(const PageRegs<F>& t, int g) {
   return t.sz[g >> 2][g & 3];
+}
+// Codes of RoPE block gr (0, 1).
+template <int F>
+__device__ __forceinline__ half8 rope_codes(const PageRegs<F>& t, int gr) {
+  if (fmt_rb(F) == 4) return codes4(t.r[gr]);
+  return codes2(t.r.x, gr);
 }
 
 // Masked page: a token with keep false gets zero (scale, zero) words, so its
 // codes contribute 0 to the scores and the tile (its score is set to -inf).
-template <int CB>
-__device__ __forceinline__ void mask_token(PageRegs<CB>& t, bool keep) {
+template <int F>
+__device__ __forceinline__ void mask_token(PageRegs<F>& t, bool keep) {
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll

@@ -145,11 +145,13 @@ struct ConvRaw {
   uint32_t r, rs;
 };
 
-template <int CB>
+// (A group of 2 or 4 blocks has one (scale, zero) word: it is repeated for
+// each of its blocks, so the tiles always hold one word per block.)
+template <int F>
 __device__ __forceinline__ void conv_load(ConvRaw& t, __amdgpu_buffer_rsrc_t rs, int slot, int j,
                                           int cq) {
-  using G = PageGeom<CB>;
-  if constexpr (CB == 4) {
+  using G = PageGeom<F>;
+  if constexpr (G::CB == 4) {
     t.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                         rs, slot * G::CC + 16 * j + 64 * cq, G::OFF_CC, 0));
   } else {
@@ -157,11 +159,23 @@ __device__ __forceinline__ void conv_load(ConvRaw& t, __amdgpu_buffer_rsrc_t rs,
         rs, slot * G::CC + 16 * j + 64 * (cq >> 1) + 8 * (cq & 1), G::OFF_CC, 0));
     t.c = (u32x4){c2.x, c2.y, 0u, 0u};
   }
-  t.s = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, slot * G::CS + 16 * cq,
-                                                                        G::OFF_CS, 0));
+  if constexpr (G::GM == 1) {
+    t.s = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        rs, slot * G::CS + 16 * cq, G::OFF_CS, 0));
+  } else if constexpr (G::GM == 2) {
+    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                  rs, slot * G::CS + 8 * cq, G::OFF_CS, 0));
+    t.s = (u32x4){w.x, w.x, w.y, w.y};
+  } else {
+    const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::CS + 4 * cq, G::OFF_CS, 0);
+    t.s = (u32x4){w, w, w, w};
+  }
   if (cq < NG_R) {
-    t.r = __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::RC + 8 * j + 4 * cq, G::OFF_RC, 0);
-    t.rs = __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::RS + 4 * cq, G::OFF_RS, 0);
+    // 4-bit: word cq of chunk j; 2-bit: both blocks share the chunk's word
+    t.r = G::RB == 4 ? __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::RC + 8 * j + 4 * cq, G::OFF_RC, 0)
+                     : __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::RC + 4 * j, G::OFF_RC, 0);
+    t.rs = __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::RS + (G::GMR == 1 ? 4 * cq : 0),
+                                                G::OFF_RS, 0);
   }
 }
 
@@ -170,7 +184,7 @@ __device__ __forceinline__ void conv_load(ConvRaw& t, __amdgpu_buffer_rsrc_t rs,
 // reconstructed values of its content groups into the value tile. A token with
 // a BF16 row (brow) takes its values with (scale, zero) = (1, 0); an invalid
 // token zeros.
-template <int CB>
+template <int F>
 __device__ __forceinline__ void convert_tok(const ConvRaw& t, _Float16* crow, uint32_t* zrow,
                                             _Float16* vrow, int j, int cq, bool mixed, bool valid,
                                             const uint16_t* brow) {
@@ -178,8 +192,8 @@ __device__ __forceinline__ void convert_tok(const ConvRaw& t, _Float16* crow, ui
   uint32_t rsw = t.rs;
   half8 c[4], r;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) c[e] = CB == 4 ? codes4(t.c[e]) : codes2(t.c[e >> 1], e & 1);
-  r = codes4(t.r);
+  for (int e = 0; e < 4; ++e) c[e] = fmt_cb(F) == 4 ? codes4(t.c[e]) : codes2(t.c[e >> 1], e & 1);
+  r = fmt_rb(F) == 4 ? codes4(t.r) : codes2(t.r, cq);
   if (mixed) {
     if (brow != nullptr) {
 #pragma unroll
@@ -302,7 +316,7 @@ __device__ __forceinline__ float row_max(float v) {
 // groups 4 cq .. 4 cq + 3, RoPE group cq) and accumulate O^T for its channels
 // 128 cq .. 128 cq + 127 of all 64 heads. Iteration k: scores of step k, PV of
 // step k - 1 and conversion of step k + 1; one barrier per iteration.
-template <int CB>
+template <int F>
 __device__ __forceinline__ void segment(WideLds& sm, const DecodeArgs& a, const SeqW& s, int v,
                                         int b, int hh, int i_begin, int n_steps, bool direct,
                                         int slot, int w, int lane) {
@@ -409,12 +423,12 @@ __device__ __forceinline__ void segment(WideLds& sm, const DecodeArgs& a, const 
     auto step_rsrc = [&](int st) {
       const int pid = __builtin_amdgcn_readfirstlane(
           st < n_steps ? *(const_i32*)(ptab + i_begin + (st >> 1)) : 0);
-      return page_rsrc<CB>(a.pages, pid, st < n_steps);
+      return page_rsrc<F>(a.pages, pid, st < n_steps);
     };
     auto load_step = [&](ConvRaw (&r)[2], int st) {
       const __amdgpu_buffer_rsrc_t rs = step_rsrc(st);
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) conv_load<CB>(r[tb], rs, ST * (st & 1) + 16 * tb + t16, j, cq);
+      for (int tb = 0; tb < 2; ++tb) conv_load<F>(r[tb], rs, ST * (st & 1) + 16 * tb + t16, j, cq);
     };
     auto convert_step = [&](const ConvRaw (&r)[2], int st) {
       const int buf = st & 1;
@@ -429,7 +443,7 @@ __device__ __forceinline__ void segment(WideLds& sm, const DecodeArgs& a, const 
         if (mixed && valid && (p < s.n_s || p >= s.lo_start))
           brow = p < s.n_s ? a.sink + ((int64_t)b * a.n_sink + p) * D_ALL
                            : a.local + ((int64_t)b * a.n_local + p % a.n_local) * D_ALL;
-        convert_tok<CB>(r[tb], sm.code[buf] + row * CT, sm.sz[buf] + row * SZT,
+        convert_tok<F>(r[tb], sm.code[buf] + row * CT, sm.sz[buf] + row * SZT,
                         sm.val[buf] + row * VT, j, cq, mixed, valid, brow);
       }
     };
@@ -531,7 +545,7 @@ __device__ __forceinline__ void segment(WideLds& sm, const DecodeArgs& a, const 
   __syncthreads();  // LDS is reused by the next segment
 }
 
-template <int CB>
+template <int F>
 __global__ __launch_bounds__(NT, 1) void decode_wide_kernel(DecodeArgs a) {
   __shared__ WideLds sm;
   const int tid = threadIdx.x;
@@ -612,7 +626,7 @@ __global__ __launch_bounds__(NT, 1) void decode_wide_kernel(DecodeArgs a) {
     const int b = v / a.s_q;
     const int n_steps = __builtin_amdgcn_readfirstlane(
         min(2 * (i_end - i_begin), (s.Lq - PAGE * i_begin + ST - 1) / ST));
-    segment<CB>(sm, a, s, v, b, hh, i_begin, n_steps, direct, v + c, w, lane);
+    segment<F>(sm, a, s, v, b, hh, i_begin, n_steps, direct, v + c, w, lane);
   }
 }
 
@@ -665,7 +679,7 @@ size_t wide_workspace_bytes(int B, int s_q) {
   return meta + slots * RG * sizeof(float) + slots * RG * D_C * sizeof(_Float16);
 }
 
-hipError_t launch_decode_wide(DecodeArgs a, void* workspace, int c_bits, hipStream_t stream) {
+hipError_t launch_decode_wide(DecodeArgs a, void* workspace, int fmt, hipStream_t stream) {
   const size_t V = (size_t)a.B * a.s_q;
   const size_t meta = (V * 8 + 255) / 256 * 256;
   const size_t slots = (size_t)NCH + V;
@@ -674,10 +688,9 @@ hipError_t launch_decode_wide(DecodeArgs a, void* workspace, int c_bits, hipStre
   a.ws_lse = reinterpret_cast<float*>(base + meta);
   a.ws_o = reinterpret_cast<_Float16*>(base + meta + slots * RG * sizeof(float));
   const dim3 grid(2 * NCH);
-  if (c_bits == 4)
-    decode_wide_kernel<4><<<grid, dim3(NT), 0, stream>>>(a);
-  else
-    decode_wide_kernel<2><<<grid, dim3(NT), 0, stream>>>(a);
+#define MLA_LAUNCH_WIDE(F) decode_wide_kernel<F><<<grid, dim3(NT), 0, stream>>>(a)
+  MLA_FOR_PACKED_FMT(fmt, MLA_LAUNCH_WIDE)
+#undef MLA_LAUNCH_WIDE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)V * RG;

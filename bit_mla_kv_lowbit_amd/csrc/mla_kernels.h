@@ -62,13 +62,14 @@ struct SplitPlan {
 SplitPlan plan_splits(int B, int H, int max_pages);
 size_t decode_workspace_bytes(int B, int H, int max_pages);
 
-hipError_t launch_write(const WriteArgs& a, int c_bits, hipStream_t stream);  // c_bits 16: BF16 pages
-hipError_t launch_decode(DecodeArgs a, int c_bits, hipStream_t stream);  // c_bits 16: BF16 pages
-hipError_t launch_qdq(const QdqArgs& a, int c_bits, hipStream_t stream);
+// fmt: a format code of mla_common.h (fmt_code), or 16 for the BF16 pages
+hipError_t launch_write(const WriteArgs& a, int fmt, hipStream_t stream);
+hipError_t launch_decode(DecodeArgs a, int fmt, hipStream_t stream);
+hipError_t launch_qdq(const QdqArgs& a, int fmt, hipStream_t stream);
 
 // 128 heads per query token (packed caches): each page is dequantized once per
 // 64 heads; work split by page weight on the device (decode_wide.hip).
 size_t wide_workspace_bytes(int B, int s_q);
-hipError_t launch_decode_wide(DecodeArgs a, void* workspace, int c_bits, hipStream_t stream);
+hipError_t launch_decode_wide(DecodeArgs a, void* workspace, int fmt, hipStream_t stream);
 
 }  // namespace mla

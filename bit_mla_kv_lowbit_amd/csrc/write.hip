@@ -34,19 +34,43 @@ __device__ __forceinline__ void quad_merge(float& lo, float& hi, int j) {
   hi = hi_b > hi_a ? hi_b : hi_a;
 }
 
-// Minimum and maximum of a group held by the 4 lanes of a quad (lane j holds
-// channels 8j..8j+7, its own extremes in lo / hi): on equal values (+0 / -0)
-// the earlier channel wins, as in a scan over the group in channel order.
-__device__ __forceinline__ void quad_extremes(float& lo, float& hi, int j) {
-  quad_merge<1>(lo, hi, j);
-  quad_merge<2>(lo, hi, j);
+// Merge with the mirrored lane of the half row (CTRL 0x141: lane i <-> 7 - i
+// within 8) or of the row (0x140: i <-> 15 - i within 16); the lanes with bit
+// M of j set hold the later channels. After the quad merges every lane of a
+// quad holds the quad's extremes, so one mirror step joins two quads, the
+// next two 8-lane halves.
+template <int CTRL, int M>
+__device__ __forceinline__ void mirror_merge(float& lo, float& hi, int j) {
+  const float plo = __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, lo), CTRL, 0xF, 0xF, false));
+  const float phi = __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, hi), CTRL, 0xF, 0xF, false));
+  const bool upper = (j & M) != 0;
+  const float lo_a = upper ? plo : lo, lo_b = upper ? lo : plo;
+  const float hi_a = upper ? phi : hi, hi_b = upper ? hi : phi;
+  lo = lo_b < lo_a ? lo_b : lo_a;
+  hi = hi_b > hi_a ? hi_b : hi_a;
 }
 
-// Asymmetric min-max quantization of one 32-channel group held by the 4
-// lanes of a quad (lane j: channels 8j .. 8j + 7 in raw, bf16): fp16 scale
-// s = (hi - lo) / (2^bits - 1) and zero z = lo (both rounded to nearest even);
-// the lane's codes q = clamp(rint((x - z) / s), 0, 2^bits - 1), all 0 when
-// s = 0. Every fp32 step matches one IEEE operation rounded to nearest even.
+// Minimum and maximum of a group held by 4 GM consecutive lanes, aligned to
+// 4 GM lanes (lane j of the group holds channels 8j..8j+7, its own extremes
+// in lo / hi): on equal values (+0 / -0) the earlier channel wins, as in a
+// scan over the group in channel order.
+template <int GM>
+__device__ __forceinline__ void group_extremes(float& lo, float& hi, int j) {
+  quad_merge<1>(lo, hi, j);
+  quad_merge<2>(lo, hi, j);
+  if constexpr (GM >= 2) mirror_merge<0x141, 4>(lo, hi, j);
+  if constexpr (GM >= 4) mirror_merge<0x140, 8>(lo, hi, j);
+}
+
+// Asymmetric min-max quantization of one group of 32 GM channels held by
+// 4 GM lanes (lane j of the group: channels 8j .. 8j + 7 in raw, bf16): fp16
+// scale s = (hi - lo) / (2^bits - 1) and zero z = lo (both rounded to nearest
+// even); the lane's codes q = clamp(rint((x - z) / s), 0, 2^bits - 1), all 0
+// when s = 0. Every fp32 step matches one IEEE operation rounded to nearest
+// even.
+template <int GM>
 __device__ __forceinline__ void quantize8(const u32x4& raw, int bits, int j, _Float16& s16,
                                           _Float16& z16, uint32_t (&q)[8]) {
   float x[8];
@@ -61,7 +85,7 @@ __device__ __forceinline__ void quantize8(const u32x4& raw, int bits, int j, _Fl
     lo = x[i] < lo ? x[i] : lo;
     hi = x[i] > hi ? x[i] : hi;
   }
-  quad_extremes(lo, hi, j);
+  group_extremes<GM>(lo, hi, j);
   const float qmax = (float)((1 << bits) - 1);
   s16 = (_Float16)__fdiv_rn(__fsub_rn(hi, lo), qmax);  // nearest even
   z16 = (_Float16)lo;
@@ -100,50 +124,62 @@ __device__ __forceinline__ void quantize8(const u32x4& raw, int bits, int j, _Fl
     q[i] = s != 0.0f ? (uint32_t)__builtin_amdgcn_fmed3f(r[i], 0.0f, qmax) : 0u;
 }
 
-// Quantize and store the 8 channels (sub-block j of group gi) one lane holds
-// of a token's content (rope false) or RoPE part, given the group's lanes in
-// its quad; also its share of the BF16 copy when the token is protected.
-template <int CB>
+// Quantize and store the 8 channels (sub-block j of 32-channel block gi) one
+// lane holds of a token's content (rope false) or RoPE part, given the lanes
+// of its group (4 per block, aligned); also its share of the BF16 copy when
+// the token is protected.
+template <int F>
 __device__ __forceinline__ void quantize_store(const WriteArgs& a, const u32x4& raw, bool rope,
                                                int gi, int j, uint8_t* base, int slot,
                                                uint16_t* keep) {
-  using G = PageGeom<CB>;
-  const int bits = rope ? 4 : CB;
+  using G = PageGeom<F>;
+  const int bits = rope ? G::RB : G::CB;
   _Float16 s16, z16;
   uint32_t q[8];
-  quantize8(raw, bits, j, s16, z16, q);
+  // lane index inside the group: content groups span GM blocks, RoPE groups GMR
+  int gsz;  // blocks per group
+  if (rope) {
+    gsz = G::GMR;
+    quantize8<G::GMR>(raw, bits, 4 * (gi % G::GMR) + j, s16, z16, q);
+  } else {
+    gsz = G::GM;
+    quantize8<G::GM>(raw, bits, 4 * (gi % G::GM) + j, s16, z16, q);
+  }
 
-  // pack (code order of the page layout): sub-block j of a group goes to chunk
-  // j of the group's chunk row; channel 8j + 2i + k sits at bit 16k + bits *
-  // (4e + i) of its 32-bit word, e = code block of the group.
-  if (rope || bits == 4) {
+  // pack (code order of the page layout, on 32-channel blocks): sub-block j of
+  // a block goes to chunk j of the block's chunk row; channel 8j + 2i + k sits
+  // at bit 16k + bits * (4e + i) of its 32-bit word, e = code block of the block.
+  if (bits == 4) {
     uint32_t v = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) v |= (q[2 * i] << (4 * i)) | (q[2 * i + 1] << (16 + 4 * i));
-    if (rope)  // 2 groups per 8-byte chunk: chunk j at 8j, word gi
+    if (rope)  // 2 blocks per 8-byte chunk: chunk j at 8j, word gi
       *reinterpret_cast<uint32_t*>(base + G::OFF_RC + slot * G::RC + 8 * j + 4 * gi) = v;
-    else  // 4 groups per 16-byte chunk: chunk (ld, j) at 16 (4 ld + j), word gi % 4
+    else  // 4 blocks per 16-byte chunk: chunk (ld, j) at 16 (4 ld + j), word gi % 4
       *reinterpret_cast<uint32_t*>(base + G::OFF_CC + slot * G::CC + 16 * (4 * (gi >> 2) + j) +
                                    4 * (gi & 3)) = v;
   } else {
-    // 8 groups per 16-byte chunk, two per word (code block e): the group owns
-    // byte e (even channels) and byte 2 + e (odd channels) of the word
+    // two blocks per word (code block e = gi mod 2): the block owns byte e
+    // (even channels) and byte 2 + e (odd channels) of the word; content: 8
+    // blocks per 16-byte chunk, RoPE: its 2 blocks in one word, chunk j at 4j
     uint32_t vlo = 0, vhi = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       vlo |= q[2 * i] << (2 * i);
       vhi |= q[2 * i + 1] << (2 * i);
     }
-    uint8_t* wp = base + G::OFF_CC + slot * G::CC + 16 * (4 * (gi >> 3) + j) + 4 * ((gi >> 1) & 3);
+    uint8_t* wp = rope ? base + G::OFF_RC + slot * G::RC + 4 * j
+                       : base + G::OFF_CC + slot * G::CC + 16 * (4 * (gi >> 3) + j) +
+                             4 * ((gi >> 1) & 3);
     const int e = gi & 1;
     wp[e] = (uint8_t)vlo;
     wp[2 + e] = (uint8_t)vhi;
   }
-  if (j == 0) {
+  if (j == 0 && gi % gsz == 0) {  // the group's first lane stores its (scale, zero)
     const uint32_t sz = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
                         ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
-    uint8_t* szdst = rope ? base + G::OFF_RS + slot * G::RS + gi * 4
-                          : base + G::OFF_CS + slot * G::CS + gi * 4;
+    uint8_t* szdst = rope ? base + G::OFF_RS + slot * G::RS + (gi / gsz) * 4
+                          : base + G::OFF_CS + slot * G::CS + (gi / gsz) * 4;
     *reinterpret_cast<uint32_t*>(szdst) = sz;
   }
   if (keep) *reinterpret_cast<u32x4*>(keep + (rope ? D_C : 0) + gi * GROUP + 8 * j) = raw;
@@ -152,7 +188,7 @@ __device__ __forceinline__ void quantize_store(const WriteArgs& a, const u32x4& 
 // Where token t goes: its page base and slot and its BF16 row (null unless
 // protected); false for a token outside the page table (or of no sequence),
 // which is dropped, never written out of bounds.
-template <int CB>
+template <int F>
 __device__ __forceinline__ bool token_dest(const WriteArgs& a, int t, uint8_t*& base, int& slot,
                                            uint16_t*& keep) {
   const int b = a.seq_idx ? a.seq_idx[t] : t;
@@ -160,7 +196,7 @@ __device__ __forceinline__ bool token_dest(const WriteArgs& a, int t, uint8_t*& 
   if (b < 0 || b >= a.B || p < 0 || p >= a.max_pages * PAGE) return false;
   const int L = a.seq_lens[b];
   const int64_t page = a.page_table[(int64_t)b * a.max_pages + p / PAGE];
-  base = a.pages + page * (int64_t)PageGeom<CB>::BYTES;
+  base = a.pages + page * (int64_t)PageGeom<F>::BYTES;
   slot = p % PAGE;
   keep = nullptr;
   if (p < a.n_sink)
@@ -178,7 +214,7 @@ __device__ __forceinline__ bool token_dest(const WriteArgs& a, int t, uint8_t*& 
 // loads of the wavefront (the tokens' indices with scalar loads, then every
 // input row) are issued before the first token is quantized, so the chain of
 // dependent reads is paid once per TW tokens.
-template <int CB>
+template <int F>
 __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
   constexpr int TW = 8;
   const int lane = threadIdx.x & 63;
@@ -202,10 +238,10 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
   bool ok[TW];
 #pragma unroll
   for (int k = 0; k < TW; ++k)
-    ok[k] = k < nt && token_dest<CB>(a, t0 + k, base[k], slot[k], keep[k]);
+    ok[k] = k < nt && token_dest<F>(a, t0 + k, base[k], slot[k], keep[k]);
 #pragma unroll
   for (int k = 0; k < TW; ++k)
-    if (ok[k]) quantize_store<CB>(a, raw[k], false, lane >> 2, lane & 3, base[k], slot[k], keep[k]);
+    if (ok[k]) quantize_store<F>(a, raw[k], false, lane >> 2, lane & 3, base[k], slot[k], keep[k]);
   // RoPE parts: the lanes of token k (8k .. 8k + 7) take its destination
   uint8_t* rb = nullptr;
   int rslot = 0;
@@ -220,7 +256,7 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
       rkeep = keep[k];
     }
   }
-  if (rok) quantize_store<CB>(a, raw[TW], true, (lane & 7) >> 2, lane & 3, rb, rslot, rkeep);
+  if (rok) quantize_store<F>(a, raw[TW], true, (lane & 7) >> 2, lane & 3, rb, rslot, rkeep);
 }
 
 // Paired BF16 cache (the unquantized baseline of the Figure 5(b) and Table 9
@@ -244,9 +280,9 @@ __global__ __launch_bounds__(256) void write_bf16_kernel(WriteArgs a) {
   row[k] = v;
 }
 
-hipError_t launch_write(const WriteArgs& a, int c_bits, hipStream_t stream) {
+hipError_t launch_write(const WriteArgs& a, int fmt, hipStream_t stream) {
   if (a.n_tokens == 0) return hipSuccess;
-  if (c_bits == 16) {
+  if (fmt == 16) {
     const int64_t total = (int64_t)a.n_tokens * (D_ALL / 8);
     write_bf16_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(a);
     return hipGetLastError();
@@ -254,30 +290,15 @@ hipError_t launch_write(const WriteArgs& a, int c_bits, hipStream_t stream) {
   const int64_t waves = ((int64_t)a.n_tokens + 7) / 8;  // 8 tokens per wavefront
   const int threads = 256;
   const int64_t blocks = (waves * 64 + threads - 1) / threads;
-  if (c_bits == 4)
-    write_kernel<4><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(a);
-  else
-    write_kernel<2><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(a);
+#define MLA_LAUNCH_WRITE(F) write_kernel<F><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(a)
+  MLA_FOR_PACKED_FMT(fmt, MLA_LAUNCH_WRITE)
+#undef MLA_LAUNCH_WRITE
   return hipGetLastError();
 }
 
-// Simulated quantize-dequantize (Figure 3 caption): one lane per 8 channels
-// (72 per token: 64 content, 8 RoPE; quads never straddle a token), the
-// writer's quantizer, then x^ = q * s + z as one fused multiply-add rounded to
-// fp32 and rounded to bf16 (nearest even); 16 B in and out per lane.
-template <int CB>
-__global__ __launch_bounds__(256) void qdq_kernel(QdqArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)a.n_tokens * (D_ALL / 8)) return;
-  const int64_t t = gid / (D_ALL / 8);
-  const int w = (int)(gid % (D_ALL / 8));
-  const bool rope = w >= D_C / 8;
-  const int wl = rope ? w - D_C / 8 : w;  // 8-channel block within the part
-  const int64_t off = rope ? t * D_R + 8 * wl : t * D_C + 8 * wl;
-  const u32x4 raw = *reinterpret_cast<const u32x4*>((rope ? a.k_rope : a.c_kv) + off);
-  _Float16 s16, z16;
-  uint32_t q[8];
-  quantize8(raw, rope ? 4 : CB, wl & 3, s16, z16, q);
+// x^ = q * s + z of 8 codes as one fused multiply-add each, rounded to fp32
+// and then to bf16 (nearest even), packed as 8 bf16.
+__device__ __forceinline__ u32x4 dequant8(const uint32_t (&q)[8], _Float16 s16, _Float16 z16) {
   const float s = (float)s16, z = (float)z16;
   u32x4 v;
 #pragma unroll
@@ -286,17 +307,49 @@ __global__ __launch_bounds__(256) void qdq_kernel(QdqArgs a) {
     const float hi = __builtin_fmaf((float)q[2 * e + 1], s, z);
     v[e] = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
   }
-  *reinterpret_cast<u32x4*>((rope ? a.out_r : a.out_c) + off) = v;
+  return v;
 }
 
-hipError_t launch_qdq(const QdqArgs& a, int c_bits, hipStream_t stream) {
+// Simulated quantize-dequantize (Figure 3 caption): the writer's wavefront
+// layout (8 tokens per wavefront: one content pass per token, lane l holding
+// channels 8l..8l+7, then one pass over the 8 tokens' RoPE parts, 8 lanes
+// each), so every group's lanes are consecutive and aligned; its quantizer,
+// then dequant8. 16 B in and out per lane and pass.
+template <int F>
+__global__ __launch_bounds__(256) void qdq_kernel(QdqArgs a) {
+  using G = PageGeom<F>;
+  constexpr int TW = 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t t0 = (int64_t)__builtin_amdgcn_readfirstlane(
+                         (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6))) * TW;
+  if (t0 >= a.n_tokens) return;
+  const int nt = (int)min((int64_t)TW, a.n_tokens - t0);
+  for (int k = 0; k < nt; ++k) {
+    const int64_t off = (t0 + k) * D_C + 8 * lane;
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(a.c_kv + off);
+    _Float16 s16, z16;
+    uint32_t q[8];
+    quantize8<G::GM>(raw, G::CB, lane & (4 * G::GM - 1), s16, z16, q);
+    *reinterpret_cast<u32x4*>(a.out_c + off) = dequant8(q, s16, z16);
+  }
+  // RoPE parts: token t0 + (lane >> 3), channels 8 (lane & 7); lanes of a token
+  // past the end read the last token (every lane takes part in the exchange)
+  const int64_t tr = t0 + (lane >> 3);
+  const int64_t off = min(tr, (int64_t)a.n_tokens - 1) * D_R + 8 * (lane & 7);
+  const u32x4 raw = *reinterpret_cast<const u32x4*>(a.k_rope + off);
+  _Float16 s16, z16;
+  uint32_t q[8];
+  quantize8<G::GMR>(raw, G::RB, lane & (4 * G::GMR - 1), s16, z16, q);
+  if (tr < a.n_tokens) *reinterpret_cast<u32x4*>(a.out_r + off) = dequant8(q, s16, z16);
+}
+
+hipError_t launch_qdq(const QdqArgs& a, int fmt, hipStream_t stream) {
   if (a.n_tokens == 0) return hipSuccess;
-  const int64_t total = (int64_t)a.n_tokens * (D_ALL / 8);
-  const dim3 grid((unsigned)((total + 255) / 256));
-  if (c_bits == 4)
-    qdq_kernel<4><<<grid, dim3(256), 0, stream>>>(a);
-  else
-    qdq_kernel<2><<<grid, dim3(256), 0, stream>>>(a);
+  const int64_t waves = (a.n_tokens + 7) / 8;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+#define MLA_LAUNCH_QDQ(F) qdq_kernel<F><<<grid, dim3(256), 0, stream>>>(a)
+  MLA_FOR_PACKED_FMT(fmt, MLA_LAUNCH_QDQ)
+#undef MLA_LAUNCH_QDQ
   return hipGetLastError();
 }
 

@@ -34,7 +34,10 @@
  *     out-of-range page-table entry, position or length is undefined behaviour.
  *   - Calls are reentrant and thread-safe.
  *
- * Quantizer (per token, per group of 32 contiguous channels; bit-exact):
+ * Quantizer (per token, per group of cfg->group contiguous channels, 32 in
+ * the C4R4 / C2R4 workloads, 64 or 128 as variants; a group never spans the
+ * content / RoPE boundary, and at group 128 the 64-channel RoPE key is one
+ * group; bit-exact):
  *   lo = min, hi = max of the group (bf16 values widened to fp32);
  *   s = fp16_rne(fp32(hi - lo) / fp32(2^b - 1)), z = fp16_rne(lo);
  *   q = 0 if s == 0, else clamp(rint_even((x - z) / s), 0, 2^b - 1) in fp32;
@@ -47,14 +50,22 @@
  *   content (s,z)  [64][16][2] fp16    at 18432 | 10240
  *   RoPE (s,z)     [64][2][2] fp16     at 22528 | 14336
  *   page bytes     23040 | 14848       (360 | 232 B per token)
- * Code order inside a token's code row (little-endian 32-bit words; channel
- * c of group g is 32 g + 8 j + 2 i + k with sub-block j, pair i = 0..3, k = 0, 1):
+ * In general the regions are, per token, d_c c_bits / 8 and d_r r_bits / 8
+ * code bytes, then one 4-byte (s, z) pair per content group and per RoPE
+ * group, each region 64 tokens long, in that order (e.g. C4R4 with groups of
+ * 64: 256 + 32 + 8 * 4 + 1 * 4 = 324 B per token; C2R2 with groups of 32:
+ * 128 + 16 + 16 * 4 + 2 * 4 = 216 B).
+ * Code order inside a token's code row (little-endian 32-bit words), the same
+ * for every group size: channel c of 32-channel block g is 32 g + 8 j + 2 i + k
+ * with sub-block j, pair i = 0..3, k = 0, 1:
  *   content, 4-bit: 16-byte chunk (j, l = g div 4) at byte 16 (4 l + j), word
  *     g mod 4, channel at bit 16 k + 4 i;
  *   content, 2-bit: 16-byte chunk (j, l = g div 8) at byte 16 (4 l + j), word
  *     (g mod 8) div 2, channel at bit 16 k + 8 (g mod 2) + 2 i;
- *   RoPE, 4-bit: 8-byte chunk j at byte 8 j, word g, channel at bit 16 k + 4 i.
- * So one 16-byte load gives the same 8 channels of 4 (or 8) groups, and even
+ *   RoPE, 4-bit: 8-byte chunk j at byte 8 j, word g, channel at bit 16 k + 4 i;
+ *   RoPE, 2-bit: 4-byte chunk j at byte 4 j (one word), channel at bit
+ *     16 k + 8 g + 2 i.
+ * So one 16-byte load gives the same 8 channels of 4 (or 8) blocks, and even
  * channels sit in the low half-word, odd ones in the high half-word.
  *
  * Protected tokens (sink / local buffers, bf16 [B][n][d_c + d_r], row =
@@ -84,8 +95,12 @@ extern "C" {
  * process ends). */
 #define MLA_LOWBIT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
-/* Cache geometry. Supported: d_c = 512, d_r = 64, c_bits in {4, 2}, r_bits = 4,
- * group = 32, page_size = 64, 0 <= n_sink <= 64, 0 <= n_local <= 256. */
+/* Cache geometry. Supported: d_c = 512, d_r = 64, c_bits in {4, 2},
+ * r_bits in {4, 2}, group in {32, 64, 128}, page_size = 64,
+ * 0 <= n_sink <= 64, 0 <= n_local <= 256. The workloads use C4R4 and C2R4
+ * (r_bits = 4, group = 32); the other bit widths and group sizes are
+ * variants of the same writer and decode (QuantMLA abstract: INT4 or INT2
+ * content with an INT4 RoPE key; 2-bit caches on the RoLaQ page). */
 typedef struct mla_lowbit_config {
   int32_t d_c;       /* content latent width */
   int32_t d_r;       /* decoupled RoPE key width */

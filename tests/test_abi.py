@@ -39,7 +39,9 @@ def test_library_exports_every_declared_symbol():
 def test_size_queries():
     assert mla.page_bytes(mla.C4R4) == 23040
     assert mla.page_bytes(mla.C2R4) == 14848
-    assert mla.page_bytes(mla.Config(group=64)) == 0
+    assert mla.page_bytes(mla.Config(group=64)) == 64 * 324
+    assert mla.page_bytes(mla.Config(c_bits=2, r_bits=2, group=128)) == 64 * 164
+    assert mla.page_bytes(mla.Config(group=48)) == 0
     ws = mla.decode_workspace_bytes(mla.C4R4, 8, 16, 512)
     assert ws > 0 and ws % 4 == 0
     assert mla.decode_workspace_bytes(mla.C4R4, 8, 24, 512) == 0  # H not a multiple of 16
@@ -48,8 +50,19 @@ def test_size_queries():
     assert "workspace" in binding.strerror(binding.EWORKSPACE)
 
 
-@pytest.mark.parametrize("bad", [dict(d_c=256), dict(d_r=32), dict(c_bits=3), dict(r_bits=2),
-                                 dict(group=16), dict(page_size=32), dict(n_sink=65),
+@pytest.mark.parametrize("c_bits,r_bits,group", [(c, r, g) for c in (4, 2) for r in (4, 2)
+                                                 for g in (32, 64, 128)])
+def test_variant_page_bytes_match_the_oracle(c_bits, r_bits, group):
+    import oracle
+    cfg = mla.Config(c_bits=c_bits, r_bits=r_bits, group=group)
+    c = cfg.c()
+    assert mla.lib().mla_lowbit_check_config(ctypes.byref(c)) == binding.OK
+    assert mla.page_bytes(cfg) == oracle.page_bytes(oracle.Cfg(c_bits=c_bits, r_bits=r_bits,
+                                                               group=group))
+
+
+@pytest.mark.parametrize("bad", [dict(d_c=256), dict(d_r=32), dict(c_bits=3), dict(r_bits=3),
+                                 dict(group=16), dict(group=256), dict(page_size=32), dict(n_sink=65),
                                  dict(n_local=257), dict(n_sink=-1)])
 def test_unsupported_configs(bad):
     c = mla.Config(**bad).c()
@@ -101,7 +114,7 @@ def test_write_validation_errors():
     assert call(sink=None) == binding.EINVAL
     assert call(max_pages=0) == binding.EINVAL
     assert call(B=0) == binding.EINVAL
-    assert call(cfg=mla.Config(r_bits=2).c()) == binding.EUNSUPPORTED
+    assert call(cfg=mla.Config(r_bits=3).c()) == binding.EUNSUPPORTED
     assert call(n=0) == binding.OK  # nothing to write
 
 

@@ -120,6 +120,25 @@ def test_qdq_bit_exact(c_bits):
     assert np.array_equal(u16(or_), rr)
 
 
+@pytest.mark.parametrize("c_bits,r_bits,group", [(4, 2, 32), (2, 2, 64), (4, 4, 128),
+                                                 (2, 4, 64), (4, 2, 128)])
+def test_qdq_bit_exact_variants(c_bits, r_bits, group):
+    """QDQ at other bit widths and group sizes (groups of 64 / 128 channels are
+    spread over 8 / 16 lanes): bit-exact with the oracle, ragged token count."""
+    cfg = mla.Config(c_bits=c_bits, r_bits=r_bits, group=group)
+    inp = synth.build_cache_inputs([203], 1, seed=60 + group + r_bits, device="cpu")
+    c = inp.c_kv.float()
+    c[0:20, 0:128] = 2.5
+    c[20:30, 128:256] = 1e-4 * torch.randn(10, 128)
+    inp.c_kv = c.to(torch.bfloat16)
+    print(f"[case] qdq c{c_bits} r{r_bits} g{group}", flush=True)
+    oc_, or_ = mla.qdq(cfg, inp.c_kv.to(DEV), inp.k_rope.to(DEV))
+    torch.cuda.synchronize()
+    rc, rr = oracle.qdq(ocfg_of(cfg), u16(inp.c_kv), u16(inp.k_rope))
+    assert np.array_equal(u16(oc_), rc)
+    assert np.array_equal(u16(or_), rr)
+
+
 def test_qdq_in_place():
     cfg = mla.C4R4
     inp = synth.build_cache_inputs([300], 1, seed=57, device="cpu")

@@ -594,3 +594,47 @@ def test_long_context_sweep_sampled(B, L):
                                             synth.SOFTMAX_SCALE)
         assert_decode_ok(out, lse, ref, ref_lse, rows=[(b, h) for h in range(H)],
                          label=f"sweep B{B} L{L} seq {b}")
+
+
+VARIANTS = [(4, 2, 32), (2, 2, 32), (4, 4, 64), (2, 4, 128), (4, 2, 128), (2, 2, 64)]
+
+
+@pytest.mark.parametrize("c_bits,r_bits,group", VARIANTS)
+def test_variant_writer_bit_exact(c_bits, r_bits, group):
+    """Other bit widths and group sizes (2-bit RoPE codes, groups of 64 and 128
+    channels): pages, sink and local buffers bit-exact with the oracle, canary
+    bytes outside the written slots kept; degenerate groups included."""
+    cfg = mla.Config(c_bits=c_bits, r_bits=r_bits, group=group)
+    lens = [700, 1, 5, 64, 65, 133, 197]
+    inp = synth.build_cache_inputs(lens, 16, seed=90 + c_bits + r_bits + group, device="cpu",
+                                   spare_pages=2)
+    c = inp.c_kv.float()
+    c[0:20, 0:128] = 1.5                           # constant groups of every size
+    c[20:30, 128:256] = -0.0
+    c[30:40, 256:384] = 1e-4 * torch.randn(10, 128)  # fp16-subnormal scales
+    inp.c_kv = c.to(torch.bfloat16)
+    print(f"[case] variant writer c{c_bits} r{r_bits} g{group}", flush=True)
+    pages, sink, local = gpu_cache(cfg, inp, len(lens), canary=0x5A)
+    torch.cuda.synchronize()
+    op, osink, olocal = oracle_cache(ocfg_of(cfg), inp, len(lens), canary=0x5A)
+    assert np.array_equal(pages.cpu().numpy(), op)
+    assert np.array_equal(u16(sink), osink)
+    assert np.array_equal(u16(local), olocal)
+
+
+@pytest.mark.parametrize("H", [16, 128])
+@pytest.mark.parametrize("c_bits,r_bits,group", VARIANTS)
+def test_variant_decode(c_bits, r_bits, group, H):
+    """The decode over the variant formats (16-head blocks and the 128-head
+    path) against the oracle: edge lengths, several pages and a ragged tail."""
+    cfg = mla.Config(c_bits=c_bits, r_bits=r_bits, group=group)
+    lens = [1, 131, 133, 197, 1000, 2500, 0, 4099]
+    inp = synth.build_cache_inputs(lens, H, seed=110 + c_bits + r_bits + group + H, device="cpu")
+    print(f"[case] variant decode c{c_bits} r{r_bits} g{group} H{H}", flush=True)
+    pages, sink, local = gpu_cache(cfg, inp, len(lens))
+    out, lse = gpu_decode(cfg, inp, pages, sink, local)
+    torch.cuda.synchronize()
+    oc = ocfg_of(cfg)
+    op, osink, olocal = oracle_cache(oc, inp, len(lens))
+    ref, ref_lse = oracle_decode(oc, inp, op, osink, olocal, synth.SOFTMAX_SCALE)
+    assert_decode_ok(out, lse, ref, ref_lse, label=f"variant c{c_bits} r{r_bits} g{group} H{H}")
