@@ -19,28 +19,26 @@
 // when no other chunk touches that sequence; combine_wide_kernel merges the
 // rest. A record per sequence names the chunks that touch it.
 //
-// A workgroup is 4 wavefronts (one per SIMD, one workgroup per CU) and walks
-// its pages 32 tokens (half a page) per step:
-//   producer  thread (token t, sub-block j, group half hf) loads its packed
-//             codes and (scale, zero) words one step ahead, turns the codes
-//             into exact fp16 integers (magic exponent) in a code tile, keeps
-//             x = c * s + z in registers and writes it to the value tile after
-//             the next barrier. A protected token's BF16 row goes to both
-//             tiles as fp16 values with (scale, zero) = (1, 0);
-//   scores    wave (head pair hp, group half gh): S = sum_g s_g (q_g . c_g) +
-//             sum_g z_g Q_g for 32 heads over 9 of the 18 groups, one
-//             v_mfma_f32_16x16x32_f16 per (16 heads, 16 tokens, group) on the
-//             exact codes, the scale applied on the VALU; the two waves of a
-//             pair exchange their partial sums through LDS, so both hold the
-//             same full scores and take the same softmax decisions;
-//   softmax   P = 2^(S scale log2e - M) against a reference max per head that
-//             moves only when a score exceeds it by more than 2^8 (then O and
-//             l are rescaled by the published factor); P to an LDS buffer;
-//   PV        wave w: O^T for channels 128 w .. 128 w + 127 of all 64 heads
-//             (128 accumulators per lane), V^T and P^T read transposed
-//             (ds_read_b64_tr_b16).
-// Three barriers per step (scores done, P ready, next tiles ready); the code
-// and scale tiles are double-buffered, the value tile is single.
+// A workgroup is 8 wavefronts (two per SIMD, one workgroup per CU) that all do
+// the same work on a step of 32 tokens (half a page):
+//   convert  each wave takes 16 tokens x a quarter of the blocks: packed
+//            codes (loaded two steps ahead) become exact fp16 integers
+//            (magic exponent) in a code tile, the scales and zero points go
+//            to their tiles, x = c * s + z to the value tile; a protected
+//            token's BF16 row enters as fp16 values with (scale, zero) = (1, 0);
+//   scores   wave (head block hb, K half kh): S = sum_g s_g (c_g . q_g) +
+//            sum_g z_g Q_g for 16 heads over 9 of the 18 blocks, one
+//            v_mfma_f32_16x16x32_f16 per (16 tokens, block) on the exact
+//            codes, the scale applied on the VALU; the two waves of a head
+//            block add their partial sums through LDS;
+//   softmax  P = 2^(S scale log2e - M) against a reference max per head that
+//            moves only when a score exceeds it by more than 2^8 (then O and
+//            l are rescaled); both waves of a head block compute the same P,
+//            which stays in registers;
+//   PV       wave (hb, kh): O^T of its 16 heads for content channels
+//            256 kh .. 256 kh + 255 (64 accumulators per lane), V^T read
+//            transposed (ds_read_b64_tr_b16), P the B operand.
+// Two barriers per step (partial scores ready; next step converted).
 #include "mla_common.h"
 #include "mla_kernels.h"
 #include "decode_ops.h"
@@ -48,33 +46,48 @@
 namespace mla {
 namespace {
 
-constexpr int NT = 512;         // threads per workgroup (8 waves, two per SIMD)
-constexpr int WR = 64;          // query rows (heads) per workgroup
-constexpr int RG = 128;         // rows per query token on this path
-constexpr int ST = 32;          // tokens per step
-constexpr int VT = D_C + 8;     // value tile row stride in halves (1040 bytes)
-constexpr int PT = WR + 8;      // P buffer row stride in halves (144 bytes)
-constexpr int NCH = 128;        // chunks of the page line (workgroups: 2 NCH)
+constexpr int NT = 512;          // threads per workgroup (8 waves, two per SIMD)
+constexpr int WR = 64;           // query rows (heads) per workgroup
+constexpr int RG = 128;          // rows per query token on this path
+constexpr int ST = 32;           // tokens per step
+constexpr int NCH = 128;         // chunks of the page line (workgroups: 2 NCH)
+constexpr int NB = NG_C + NG_R;  // 18 blocks of 32 channels per token ([c | k_rope])
+constexpr int KH = 9;            // blocks per K half: content 8 kh .. 8 kh + 7 and RoPE block kh
+// Row strides in halves. Code tile: 292 dwords (36 mod 64), so 16 consecutive
+// token rows read or written 16 bytes per lane hit distinct banks. Value tile:
+// 268 dwords (12 mod 64), distinct banks for 16 consecutive rows of 16-byte
+// stores and for the 4 consecutive rows of a transposing read.
+constexpr int CT = D_ALL + 8;
+constexpr int VT = D_C + 24;
+// z tile row: 8 words per block quarter q (the (z, z) words of content blocks
+// 4q .. 4q + 3, then RoPE block q for q < 2), padded to 36 words (36 mod 64:
+// 16 consecutive rows hit distinct banks); scale tile rows are ordered the
+// same way (5 per quarter).
+constexpr int ZW = 36;
+constexpr int NSR = 20;          // scale tile rows
 
-constexpr int CT = D_ALL + 8;   // code tile row stride in halves (1168 bytes)
-constexpr int SZT = 20;         // (scale, zero) words per token row (18 used)
-
-// Double-buffered by step parity. In iteration k the score waves read the code
-// and (scale, zero) tiles of step k and write P of step k, while the PV waves
-// read the value tile and P of step k - 1 and fill the code, (scale, zero) and
-// value tiles of step k + 1 (each PV wave only its own value columns).
+// In iteration k the scores of step k read the code, scale and z tiles before
+// the first barrier; after it every wave runs the PV product of step k on
+// value buffer k & 1 and then converts step k + 1 into the code, scale and z
+// tiles and value buffer (k + 1) & 1, which the second barrier publishes.
 struct WideLds {
-  _Float16 code[2][ST * CT];     // fp16 codes (or BF16-row values) of 18 groups, token-major
-  uint32_t sz[2][ST * SZT];      // (scale, zero) fp16 pairs per token and group
-  _Float16 val[2][ST * VT];      // reconstructed content values, token-major
-  _Float16 p[2][ST * PT];        // P: token rows x 64 heads
-  float alpha[2][WR];            // rescale factor of each head's moved reference
-  int flag[2][4];                // per head block: its reference moved in that step
-  float lsum[WR];                // sum of P per head
-  float mref[WR];                // final reference max per head
+  _Float16 code[ST * CT];          // exact codes (or BF16-row values) of the 18 blocks, token-major
+  _Float16 val[2][ST * VT];        // reconstructed content values, token-major
+  _Float16 scl[NSR][ST];           // fp16 scale per block (row order above) and token (order below)
+  uint32_t zop[ST * ZW];           // per token: (z, z) words, layout above
+  float4v xs[NT / 64][2][64];      // each wave's partial scores [token block][lane]
   int seg_first, seg_last, p_first;
   int scan[NT / 64];
 };
+
+// Scale tile row of content block g (0..15) and of RoPE block NG_C + q.
+__device__ __forceinline__ int scale_row(int g) { return g < NG_C ? 5 * (g >> 2) + (g & 3) : 5 * (g - NG_C) + 4; }
+
+// Position in a scale row of token 16 tb + r (r < 16): the 8 tokens whose
+// scores a lane holds (rows 4 (r / 4) .. + 3 of both token blocks) are adjacent.
+__device__ __forceinline__ int scale_pos(int row) {
+  return 8 * ((row & 15) >> 2) + 4 * (row >> 4) + (row & 3);
+}
 
 // Weight of the pages of one (sequence, query token): 2 per page, 1 more for a
 // page holding BF16 rows (the sink page and the window pages).
@@ -170,30 +183,32 @@ __device__ __forceinline__ void conv_load(ConvRaw& t, __amdgpu_buffer_rsrc_t rs,
     const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::CS + 4 * cq, G::OFF_CS, 0);
     t.s = (u32x4){w, w, w, w};
   }
-  if (cq < NG_R) {
-    // 4-bit: word cq of chunk j; 2-bit: both blocks share the chunk's word
-    t.r = G::RB == 4 ? __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::RC + 8 * j + 4 * cq, G::OFF_RC, 0)
-                     : __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::RC + 4 * j, G::OFF_RC, 0);
-    t.rs = __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::RS + (G::GMR == 1 ? 4 * cq : 0),
-                                                G::OFF_RS, 0);
-  }
+  // RoPE block cq (used for cq < 2; the other quarters load block cq - 2 too,
+  // so the loads are unconditional and the prefetch registers need no merge)
+  const int rq = cq & 1;
+  // 4-bit: word rq of chunk j; 2-bit: both blocks share the chunk's word
+  t.r = G::RB == 4 ? __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::RC + 8 * j + 4 * rq, G::OFF_RC, 0)
+                   : __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::RC + 4 * j, G::OFF_RC, 0);
+  t.rs = __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::RS + (G::GMR == 1 ? 4 * rq : 0),
+                                              G::OFF_RS, 0);
 }
 
-// One converter lane's share of a step: codes of its groups into the code
-// tile, (scale, zero) words into their tile (lanes j = 0), and the
-// reconstructed values of its content groups into the value tile. A token with
-// a BF16 row (brow) takes its values with (scale, zero) = (1, 0); an invalid
+// One converter lane's share of a step (token row `row` of the step, sub-block
+// j, block quarter cq): exact fp16 codes of blocks 4 cq .. 4 cq + 3 (and RoPE
+// block cq when cq < 2) into the code tile; for j = 0 the blocks' fp16 scales
+// and (z, z) words into the scale and z tiles; the reconstructed values
+// x = c * s + z of its 4 content blocks into value buffer buf. A token with a
+// BF16 row (brow) takes its values with (scale, zero) = (1, 0); an invalid
 // token zeros.
 template <int F>
-__device__ __forceinline__ void convert_tok(const ConvRaw& t, _Float16* crow, uint32_t* zrow,
-                                            _Float16* vrow, int j, int cq, bool mixed, bool valid,
-                                            const uint16_t* brow) {
+__device__ __forceinline__ void convert_tok(const ConvRaw& t, WideLds& sm, int buf, int row, int j,
+                                            int cq, bool mixed, bool valid, const uint16_t* brow) {
   u32x4 sw = t.s;
   uint32_t rsw = t.rs;
   half8 c[4], r;
 #pragma unroll
   for (int e = 0; e < 4; ++e) c[e] = fmt_cb(F) == 4 ? codes4(t.c[e]) : codes2(t.c[e >> 1], e & 1);
-  r = fmt_rb(F) == 4 ? codes4(t.r) : codes2(t.r, cq);
+  r = fmt_rb(F) == 4 ? codes4(t.r) : codes2(t.r, cq & 1);
   if (mixed) {
     if (brow != nullptr) {
 #pragma unroll
@@ -215,332 +230,274 @@ __device__ __forceinline__ void convert_tok(const ConvRaw& t, _Float16* crow, ui
       rsw = 0u;
     }
   }
+  _Float16* crow = sm.code + row * CT;
+  _Float16* vrow = sm.val[buf] + row * VT;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int g = 4 * cq + e;
-    *reinterpret_cast<half8*>(crow + GROUP * g + 8 * j) = c[e];
-    *reinterpret_cast<half8*>(vrow + GROUP * g + 8 * j) = reconstruct(c[e], sw[e]);
+    *reinterpret_cast<half8*>(crow + GROUP * (4 * cq + e) + 8 * j) = c[e];
+    *reinterpret_cast<half8*>(vrow + GROUP * (4 * cq + e) + 8 * j) = reconstruct(c[e], sw[e]);
   }
   if (cq < NG_R) *reinterpret_cast<half8*>(crow + D_C + GROUP * cq + 8 * j) = r;
   if (j == 0) {
-    *reinterpret_cast<u32x4*>(zrow + 4 * cq) = sw;
-    if (cq < NG_R) zrow[NG_C + cq] = rsw;
+    _Float16* sc = &sm.scl[5 * cq][scale_pos(row)];
+    uint32_t* zr = sm.zop + row * ZW + 8 * cq;
+    u32x4 zz;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sc[ST * e] = as_h2(sw[e]).x;
+      zz[e] = (sw[e] & 0xffff0000u) | (sw[e] >> 16);  // (z, z)
+    }
+    *reinterpret_cast<u32x4*>(zr) = zz;
+    if (cq < NG_R) {
+      sc[ST * 4] = as_h2(rsw).x;
+      zr[4] = (rsw & 0xffff0000u) | (rsw >> 16);
+    }
   }
 }
 
-// Scores of 16 heads for the two token blocks of a step (lane: token t16 of
-// each block, sub-block j), from the code and (scale, zero) tiles, exactly per
-// group: integer codes (or BF16-row values with scale 1) are the MFMA B
-// operand, each group's product is scaled on the VALU one group later, and the
-// zero points enter through two MFMAs against the group sums of q (hi and lo
-// fp16 parts). Both blocks go through the group loop together.
-__device__ __forceinline__ void step_scores(const _Float16* code, const uint32_t* sz,
-                                            const half8 (&qA)[18], const half8& qz1,
-                                            const half8& qz2, int j, int t16, float4v (&S)[2]) {
+// Block k (0..8) of K half kh: content block 8 kh + k, then RoPE block 16 + kh.
+__device__ __forceinline__ int half_block(int kh, int k) { return k < 8 ? 8 * kh + k : NG_C + kh; }
+
+// Partial scores of 16 heads (lane: head t16, rows 4 j .. 4 j + 3 of each
+// token block) over the wave's K half (its 9 blocks), exactly per block:
+// integer codes (or BF16-row values with scale 1) are the MFMA A operand, q the
+// B operand, and each block's product is scaled on the VALU; the zero points
+// enter through one MFMA per token block whose A operand holds (z, z) per block
+// against the (hi, lo) fp16 parts of the group sums of q.
+__device__ __forceinline__ void step_scores(const WideLds& sm, int kh,
+                                            const half8 (&qA)[KH], const half8& qz, int j,
+                                            int t16, float4v (&S)[2]) {
   const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
-  float sc[2][NG_C + NG_R];
+  const _Float16* c0 = sm.code + t16 * CT + 8 * j;
+  const _Float16* c1 = c0 + 16 * CT;
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
-    const uint32_t* zrow = sz + (16 * tb + t16) * SZT;
-    u32x4 w4[5];
-#pragma unroll
-    for (int k = 0; k < 5; ++k) w4[k] = *reinterpret_cast<const u32x4*>(zrow + 4 * k);
-    uint32_t wd[20];
-#pragma unroll
-    for (int k = 0; k < 5; ++k) {
-      wd[4 * k] = w4[k].x;
-      wd[4 * k + 1] = w4[k].y;
-      wd[4 * k + 2] = w4[k].z;
-      wd[4 * k + 3] = w4[k].w;
-    }
-#pragma unroll
-    for (int g = 0; g < NG_C + NG_R; ++g) sc[tb][g] = (float)as_h2(wd[g]).x;
-    // z operands (K slot 8 j + i): zb1 holds the z of content groups 0..7 in
-    // lanes j < 2 and the RoPE groups' z in slots 0, 1 of lanes j >= 2; zb2 the
-    // z of content groups 8..15
-    const bool lowj = j < 2;
-    const uint32_t rz = z_pair(wd[16], wd[17]);
-    const u32x4 z1 = {lowj ? z_pair(wd[0], wd[1]) : rz, lowj ? z_pair(wd[2], wd[3]) : 0u,
-                      lowj ? z_pair(wd[4], wd[5]) : 0u, lowj ? z_pair(wd[6], wd[7]) : 0u};
-    const u32x4 z2 = {z_pair(wd[8], wd[9]), z_pair(wd[10], wd[11]), z_pair(wd[12], wd[13]),
-                      z_pair(wd[14], wd[15])};
-    S[tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qz1, __builtin_bit_cast(half8, z1), zero4, 0, 0, 0);
-    S[tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qz2, __builtin_bit_cast(half8, z2), S[tb], 0, 0, 0);
+    // z operand: quarters 2 kh and 2 kh + 1 (j = 0, 1), the RoPE block's
+    // word (j = 2; in quarter kh), zeros (j = 3)
+    const uint32_t* zr = sm.zop + (16 * tb + t16) * ZW;
+    u32x4 zw = *reinterpret_cast<const u32x4*>(zr + (j < 2 ? 16 * kh + 8 * j : 8 * kh + 4));
+    if (j >= 2) zw = (u32x4){j == 2 ? zw[0] : 0u, 0u, 0u, 0u};
+    S[tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, zw), qz, zero4, 0, 0, 0);
   }
-  const _Float16* c0 = code + t16 * CT + 8 * j;
-  const _Float16* c1 = code + (16 + t16) * CT + 8 * j;
-  // B operands read PF groups ahead of their MFMAs (LDS latency)
-  constexpr int PF = 6;
-  half8 Bw[PF][2];
+  // A operands and scales read PF blocks ahead of their MFMAs (LDS latency)
+  constexpr int PF = 2;
+  half8 Aw[PF][2], Sw[PF];
 #pragma unroll
-  for (int g = 0; g < PF; ++g) {
-    Bw[g][0] = *reinterpret_cast<const half8*>(c0 + GROUP * g);
-    Bw[g][1] = *reinterpret_cast<const half8*>(c1 + GROUP * g);
+  for (int k = 0; k < PF; ++k) {
+    Aw[k][0] = *reinterpret_cast<const half8*>(c0 + GROUP * half_block(kh, k));
+    Aw[k][1] = *reinterpret_cast<const half8*>(c1 + GROUP * half_block(kh, k));
+    Sw[k] = *reinterpret_cast<const half8*>(sm.scl[scale_row(half_block(kh, k))] + 8 * j);
   }
-  float4v Dp0 = zero4, Dp1 = zero4;
 #pragma unroll
-  for (int g = 0; g < NG_C + NG_R; ++g) {
-    const half8 B0 = Bw[g % PF][0];
-    const half8 B1 = Bw[g % PF][1];
-    if (g + PF < NG_C + NG_R) {
-      const int gn = g + PF;
-      const int ch = gn < NG_C ? GROUP * gn : D_C + GROUP * (gn - NG_C);
-      Bw[g % PF][0] = *reinterpret_cast<const half8*>(c0 + ch);
-      Bw[g % PF][1] = *reinterpret_cast<const half8*>(c1 + ch);
+  for (int k = 0; k < KH; ++k) {
+    const half8 A0 = Aw[k % PF][0], A1 = Aw[k % PF][1], sc = Sw[k % PF];
+    if (k + PF < KH) {
+      Aw[k % PF][0] = *reinterpret_cast<const half8*>(c0 + GROUP * half_block(kh, k + PF));
+      Aw[k % PF][1] = *reinterpret_cast<const half8*>(c1 + GROUP * half_block(kh, k + PF));
+      Sw[k % PF] = *reinterpret_cast<const half8*>(sm.scl[scale_row(half_block(kh, k + PF))] + 8 * j);
     }
-    const float4v D0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[g], B0, zero4, 0, 0, 0);
-    const float4v D1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[g], B1, zero4, 0, 0, 0);
-    if (g > 0) {
-      S[0] += sc[0][g - 1] * Dp0;
-      S[1] += sc[1][g - 1] * Dp1;
+    const float4v D0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qA[k], zero4, 0, 0, 0);
+    const float4v D1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qA[k], zero4, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      S[0][i] += (float)sc[i] * D0[i];
+      S[1][i] += (float)sc[4 + i] * D1[i];
     }
-    Dp0 = D0;
-    Dp1 = D1;
   }
-  S[0] += sc[0][NG_C + NG_R - 1] * Dp0;
-  S[1] += sc[1][NG_C + NG_R - 1] * Dp1;
 }
 
-// Row maximum over the 16 lanes of a row (DPP).
-__device__ __forceinline__ float row_max(float v) {
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true)));
-  return v;
-}
-
-// One segment (pages [i_begin, i_begin + n_steps / 2) of sequence v, rows
-// 64 hh .. 64 hh + 63). Waves 0..3 score head block hb = w over every group;
-// waves 4..7 own channel quarter cq = w - 4: they convert its codes (content
-// groups 4 cq .. 4 cq + 3, RoPE group cq) and accumulate O^T for its channels
-// 128 cq .. 128 cq + 127 of all 64 heads. Iteration k: scores of step k, PV of
-// step k - 1 and conversion of step k + 1; one barrier per iteration.
+// One segment: pages [i_begin, i_begin + n_steps / 2) of (sequence, query
+// token) v, heads 64 hh .. 64 hh + 63. Wave w scores head block hb = w & 3
+// over K half kh = w >> 2 and accumulates O^T of those 16 heads for content
+// channels 256 kh .. 256 kh + 255; it also converts token block w >> 2, block
+// quarter w & 3 of every step. The two waves of a head block add their
+// partial scores through LDS (the same sum in both, so both take the same
+// softmax decisions and hold the same P, which stays in registers as the B
+// operand of the PV product). Iteration k: scores of step k, barrier, softmax
+// and PV of step k, conversion of step k + 1, barrier.
 template <int F>
 __device__ __forceinline__ void segment(WideLds& sm, const DecodeArgs& a, const SeqW& s, int v,
                                         int b, int hh, int i_begin, int n_steps, bool direct,
                                         int slot, int w, int lane) {
   const int j = lane >> 4, t16 = lane & 15;
+  const int hb = w & 3, kh = w >> 2;
+  const int crow = 16 * (w >> 2) + t16, cq = w & 3;  // converter: token row, block quarter
   const int* ptab = a.page_table + (int64_t)b * a.max_pages;
   auto step_p0 = [&](int st) { return PAGE * (i_begin + (st >> 1)) + ST * (st & 1); };
-  if (w < 4) {
-    // ================= score wave: 16 heads, all 18 groups =================
-    const int hb = w;
-    const float sl2 = a.scale_log2;
-    half8 qA[NG_C + NG_R];
-    half8 qz1, qz2;
-    {
-      const int64_t row = (int64_t)v * RG + WR * hh + 16 * hb + t16;
+  auto step_rsrc = [&](int st) {
+    const int pid = __builtin_amdgcn_readfirstlane(
+        st < n_steps ? *(const_i32*)(ptab + i_begin + (st >> 1)) : 0);
+    return page_rsrc<F>(a.pages, pid, st < n_steps);
+  };
+  auto load_step = [&](ConvRaw& r, int st) {
+    conv_load<F>(r, step_rsrc(st), ST * (st & 1) + crow, j, cq);
+  };
+  auto convert_step = [&](const ConvRaw& r, int st) {
+    const int p0 = step_p0(st);
+    const bool mixed = p0 < s.n_s || p0 + ST > min(s.lo_start, s.Lq);
+    const int p = p0 + crow;
+    const bool valid = p < s.Lq;
+    const uint16_t* brow = nullptr;
+    if (mixed && valid && (p < s.n_s || p >= s.lo_start))
+      brow = p < s.n_s ? a.sink + ((int64_t)b * a.n_sink + p) * D_ALL
+                       : a.local + ((int64_t)b * a.n_local + p % a.n_local) * D_ALL;
+    convert_tok<F>(r, sm, st & 1, crow, j, cq, mixed, valid, brow);
+  };
+
+  // ---- Q operands of the wave's 9 blocks and its z operand ----
+  const float sl2 = a.scale_log2;
+  const int64_t qrow = (int64_t)v * RG + WR * hh + 16 * hb + t16;
+  half8 qA[KH];
+  half8 qz;
+  {
 #pragma unroll
-      for (int g = 0; g < NG_C + NG_R; ++g) {
-        const uint16_t* src = g < NG_C ? a.q_lat + row * D_C + GROUP * g + 8 * j
-                                       : a.q_rope + row * D_R + GROUP * (g - NG_C) + 8 * j;
-        qA[g] = bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(src));
-      }
-      // group sums Q_g of head t16 (one MFMA with a ones operand); the z
-      // operands hold content groups 0..7 (lanes j < 2, else the RoPE groups)
-      // and 8..15 in fp16 hi (j even) and lo (j odd) parts
-      const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
-      const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
-      float qs[NG_C + NG_R];
+    for (int k = 0; k < KH; ++k) {
+      const int g = half_block(kh, k);
+      const uint16_t* src = g < NG_C ? a.q_lat + qrow * D_C + GROUP * g + 8 * j
+                                     : a.q_rope + qrow * D_R + GROUP * (g - NG_C) + 8 * j;
+      qA[k] = bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(src));
+    }
+    // group sums of head t16 (one MFMA with a ones operand each); the z
+    // operand word 4 j + e of the lane holds (hi, lo) of the sum of half block
+    // 4 j + e (j < 2: content blocks; word 8: the RoPE block)
+    const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+    const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
+    float qs[KH];
 #pragma unroll
-      for (int g = 0; g < NG_C + NG_R; ++g)
-        qs[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, qA[g], zero4, 0, 0, 0)[0];
-      const bool lo_part = (j & 1) != 0, lowj = j < 2;
+    for (int k = 0; k < KH; ++k)
+      qs[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, qA[k], zero4, 0, 0, 0)[0];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v1 = lowj ? qs[i] : (i < NG_R ? qs[NG_C + i] : 0.f);
-        const float v2 = lowj ? qs[8 + i] : 0.f;
-        const _Float16 h1 = (_Float16)v1, h2 = (_Float16)v2;
-        qz1[i] = lo_part ? (_Float16)(v1 - (float)h1) : h1;
-        qz2[i] = lo_part ? (_Float16)(v2 - (float)h2) : h2;
+    for (int e = 0; e < 4; ++e) {
+      const float q = j == 0 ? qs[e] : j == 1 ? qs[4 + e] : (j == 2 && e == 0) ? qs[8] : 0.f;
+      const _Float16 hi = (_Float16)q;
+      qz[2 * e] = hi;
+      qz[2 * e + 1] = (_Float16)(q - (float)hi);
+    }
+  }
+
+  // ---- raw codes of steps of parity 0 and 1, loaded two iterations ahead ----
+  ConvRaw raw0, raw1;
+  load_step(raw0, 0);
+  load_step(raw1, 1);
+  convert_step(raw0, 0);
+  load_step(raw0, 2);
+  float4v O[16];  // channel 256 kh + 16 cb + 4 j + i of head t16
+#pragma unroll
+  for (int cb = 0; cb < 16; ++cb) O[cb] = (float4v){0.f, 0.f, 0.f, 0.f};
+  float M = M_NONE;  // reference max of head t16 (log2 units)
+  float l = 0.f;     // sum of P over the lane's tokens
+  const int tr_lo = (4 * j + (t16 >> 2)) * VT + 4 * (t16 & 3) + 256 * kh;
+  const int tr_hi = tr_lo + 16 * VT;
+  __syncthreads();  // step 0 converted
+
+  // One iteration; rnext holds the raw codes of step it + 1 and is reloaded
+  // with step it + 3 (the loads are unconditional: past the last step the page
+  // descriptor has an empty range). Called with raw1 and raw0 in turn, so each
+  // prefetch lands in fixed registers.
+  auto iteration = [&](int it, ConvRaw& rnext) {
+    const int buf = it & 1;
+    const int p0 = step_p0(it);
+    float4v S[2];
+    step_scores(sm, kh, qA, qz, j, t16, S);
+    sm.xs[w][0][lane] = S[0];
+    sm.xs[w][1][lane] = S[1];
+    __syncthreads();  // partial scores of both K halves
+    S[0] += sm.xs[w ^ 4][0][lane];
+    S[1] += sm.xs[w ^ 4][1][lane];
+    // ---- softmax over the step's 32 tokens (the same in both waves of the pair) ----
+    bool big = false;
+    float u[2][4], t[2][4];  // scores in log2 units (invalid: -inf) and u - M
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool valid = p0 + 16 * tb + 4 * j + i < s.Lq;
+        u[tb][i] = valid ? S[tb][i] * sl2 : -INFINITY;
+        t[tb][i] = u[tb][i] - M;
+        big |= t[tb][i] > TAU;
       }
     }
-    float4v M = {M_NONE, M_NONE, M_NONE, M_NONE};  // reference max of heads 4 j + i
-    float4v l = {0.f, 0.f, 0.f, 0.f};              // sum of P over the lane's tokens
-    __syncthreads();  // step 0 converted
-    for (int it = 0; it <= n_steps; ++it) {
-      if (it < n_steps) {
-        const int buf = it & 1;
-        const int p0 = step_p0(it);
-        float4v S[2];
-        step_scores(sm.code[buf], sm.sz[buf], qA, qz1, qz2, j, t16, S);
-        // ---- softmax over the step's 32 tokens, in the wave ----
-        bool big = false;
-        float4v u[2], t[2];  // scores in log2 units (invalid: -inf) and u - M
+    if (__builtin_amdgcn_ballot_w64(big) != 0) {
+      // the step's maximum per head becomes the reference (lanes t16 + 16 j
+      // hold the same head)
+      float m8 = u[0][0];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const bool valid = p0 + 16 * tb + t16 < s.Lq;
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            u[tb][i] = valid ? S[tb][i] * sl2 : -INFINITY;
-            t[tb][i] = u[tb][i] - M[i];
-            big |= t[tb][i] > TAU;
-          }
-        }
-        const bool move = __builtin_amdgcn_ballot_w64(big) != 0;
-        if (move) {
-          // the step's maximum per head becomes the reference
-          float4v mn, al;
+        for (int i = 0; i < 4; ++i) m8 = fmaxf(m8, u[tb][i]);
+      m8 = fmaxf(m8, __shfl_xor(m8, 16, 64));
+      m8 = fmaxf(m8, __shfl_xor(m8, 32, 64));
+      const float mn = fmaxf(M, m8);
+      const float al = __builtin_amdgcn_exp2f(M - mn);
+      l *= al;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            mn[i] = fmaxf(M[i], row_max(fmaxf(u[0][i], u[1][i])));
-            al[i] = __builtin_amdgcn_exp2f(M[i] - mn[i]);
+      for (int cb = 0; cb < 16; ++cb) O[cb] *= al;
+      M = mn;
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) t[tb][i] = u[tb][i] - mn[i];
-          }
-          l *= al;
-          M = mn;
-          if (t16 == 0) *reinterpret_cast<float4v*>(sm.alpha[buf] + 16 * hb + 4 * j) = al;
-        }
-        if (lane == 0) sm.flag[buf][hb] = move ? 1 : 0;
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          float4v pv;
+        for (int i = 0; i < 4; ++i) t[tb][i] = u[tb][i] - M;
+    }
+    half8 pB;  // K slot 4 tb + i: token 16 tb + 4 j + i
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(t[tb][i]);
-          l += pv;
-          u32x2 ph;
-          ph.x = as_u32((half2v){(_Float16)pv[0], (_Float16)pv[1]});
-          ph.y = as_u32((half2v){(_Float16)pv[2], (_Float16)pv[3]});
-          *reinterpret_cast<u32x2*>(sm.p[buf] + (16 * tb + t16) * PT + 16 * hb + 4 * j) = ph;
-        }
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(t[tb][i]);
+        l += pv;
+        pB[4 * tb + i] = (_Float16)pv;
       }
-      __syncthreads();
-    }
-    // sum of P and reference max per head for the PV waves
-    float4v l4 = l;
+    // ---- PV: O^T += V^T P over the step's 32 tokens ----
+    const _Float16* vt = sm.val[buf];
+    half8 av = tr_pair(vt + tr_lo, vt + tr_hi);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) l4[i] = row_sum(l4[i]);
-    if (t16 == 0) {
-      *reinterpret_cast<float4v*>(sm.lsum + 16 * hb + 4 * j) = l4;
-      *reinterpret_cast<float4v*>(sm.mref + 16 * hb + 4 * j) = M;
+    for (int cb = 0; cb < 16; ++cb) {
+      const half8 cur = av;
+      if (cb + 1 < 16) av = tr_pair(vt + tr_lo + 16 * (cb + 1), vt + tr_hi + 16 * (cb + 1));
+      O[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur, pB, O[cb], 0, 0, 0);
     }
-    __syncthreads();
+    // the next step into the code, scale and z tiles (every wave's scores of
+    // this step are done) and the other value buffer (last read by the PV
+    // product of step it - 1)
+    if (it + 1 < n_steps) convert_step(rnext, it + 1);
+    load_step(rnext, it + 3);
+    __syncthreads();  // step it + 1 converted; every wave is done with the partials
+  };
+  for (int it = 0; it < n_steps; it += 2) {
+    iteration(it, raw1);
+    if (it + 1 < n_steps) iteration(it + 1, raw0);
+  }
+
+  // ---- normalize and write: out directly, or a partial for the combine ----
+  float lt = l + __shfl_xor(l, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse_v = lt > 0.f ? (M + __log2f(lt)) * LN2 : -INFINITY;
+  const int h = 16 * hb + t16;  // row within the workgroup's 64
+  const int64_t orow = (int64_t)v * RG + WR * hh + h;
+  if (direct) {
+    uint16_t* dst = a.out + orow * D_C + 256 * kh + 4 * j;
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) {
+      const float4v o = O[cb] * inv;
+      u32x2 pk;
+      pk.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
+      pk.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+      *reinterpret_cast<u32x2*>(dst + 16 * cb) = pk;
+    }
+    if (kh == 0 && j == 0) a.lse[orow] = lse_v;
   } else {
-    // ======== converter + PV wave: channel quarter cq, all 64 heads ========
-    const int cq = w - 4;
-    auto step_rsrc = [&](int st) {
-      const int pid = __builtin_amdgcn_readfirstlane(
-          st < n_steps ? *(const_i32*)(ptab + i_begin + (st >> 1)) : 0);
-      return page_rsrc<F>(a.pages, pid, st < n_steps);
-    };
-    auto load_step = [&](ConvRaw (&r)[2], int st) {
-      const __amdgpu_buffer_rsrc_t rs = step_rsrc(st);
+    const int64_t prow = (int64_t)slot * RG + WR * hh + h;
+    _Float16* dst = a.ws_o + prow * D_C + 256 * kh + 4 * j;
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) conv_load<F>(r[tb], rs, ST * (st & 1) + 16 * tb + t16, j, cq);
-    };
-    auto convert_step = [&](const ConvRaw (&r)[2], int st) {
-      const int buf = st & 1;
-      const int p0 = step_p0(st);
-      const bool mixed = p0 < s.n_s || p0 + ST > min(s.lo_start, s.Lq);
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int row = 16 * tb + t16;
-        const int p = p0 + row;
-        const bool valid = p < s.Lq;
-        const uint16_t* brow = nullptr;
-        if (mixed && valid && (p < s.n_s || p >= s.lo_start))
-          brow = p < s.n_s ? a.sink + ((int64_t)b * a.n_sink + p) * D_ALL
-                           : a.local + ((int64_t)b * a.n_local + p % a.n_local) * D_ALL;
-        convert_tok<F>(r[tb], sm.code[buf] + row * CT, sm.sz[buf] + row * SZT,
-                        sm.val[buf] + row * VT, j, cq, mixed, valid, brow);
-      }
-    };
-    // raw codes of steps of parity 0 and 1, loaded two iterations ahead
-    ConvRaw raw0[2], raw1[2];
-    load_step(raw0, 0);
-    load_step(raw1, 1);
-    convert_step(raw0, 0);
-    load_step(raw0, 2);
-    float4v O[8][4];  // [channel block][head block]: channel 128 cq + 16 cb + 4 j + i, head 16 k + t16
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) O[cb][k] = (float4v){0.f, 0.f, 0.f, 0.f};
-    const int trow = 8 * j + 2 * (t16 >> 2);
-    __syncthreads();  // step 0 converted
-    for (int it = 0; it <= n_steps; ++it) {
-      if (it >= 1) {
-        const int buf = (it - 1) & 1;
-        const int4 fl = *reinterpret_cast<const int4*>(sm.flag[buf]);
-        if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
-          const int fv[4] = {fl.x, fl.y, fl.z, fl.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            if (!fv[k]) continue;
-            const float al = sm.alpha[buf][16 * k + t16];
-#pragma unroll
-            for (int cb = 0; cb < 8; ++cb) O[cb][k] *= al;
-          }
-        }
-        half8 pB[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          pB[k] = tr_pair(sm.p[buf] + trow * PT + 16 * k + 4 * (t16 & 3),
-                          sm.p[buf] + (trow + 1) * PT + 16 * k + 4 * (t16 & 3));
-        const _Float16* vt = sm.val[buf];
-        half8 av = tr_pair(vt + trow * VT + 128 * cq + 4 * (t16 & 3),
-                           vt + (trow + 1) * VT + 128 * cq + 4 * (t16 & 3));
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          const half8 cur = av;
-          if (cb + 1 < 8) {
-            const int col = 128 * cq + 16 * (cb + 1) + 4 * (t16 & 3);
-            av = tr_pair(vt + trow * VT + col, vt + (trow + 1) * VT + col);
-          }
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            O[cb][k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur, pB[k], O[cb][k], 0, 0, 0);
-        }
-      }
-      // the next step into the other buffers (this wave's value columns of
-      // buffer (k + 1) & 1 were last read by its own PV just above)
-      if (it + 1 < n_steps) {
-        if ((it + 1) & 1) {
-          convert_step(raw1, it + 1);
-          load_step(raw1, it + 3);
-        } else {
-          convert_step(raw0, it + 1);
-          load_step(raw0, it + 3);
-        }
-      }
-      __syncthreads();
+    for (int cb = 0; cb < 16; ++cb) {
+      const float4v o = O[cb] * inv;
+      u32x2 pk;
+      pk.x = as_u32((half2v){(_Float16)o[0], (_Float16)o[1]});
+      pk.y = as_u32((half2v){(_Float16)o[2], (_Float16)o[3]});
+      *reinterpret_cast<u32x2*>(dst + 16 * cb) = pk;
     }
-    __syncthreads();  // sums and maxima of the score waves
-    // ---- normalize and write: out directly, or a partial for the combine ----
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int h = 16 * k + t16;  // row within the workgroup's 64
-      const float lt = sm.lsum[h];
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const float lse_v = lt > 0.f ? (sm.mref[h] + __log2f(lt)) * LN2 : -INFINITY;
-      const int64_t orow = (int64_t)v * RG + WR * hh + h;
-      if (direct) {
-        uint16_t* dst = a.out + orow * D_C + 128 * cq + 4 * j;
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          const float4v o = O[cb][k] * inv;
-          u32x2 pk;
-          pk.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
-          pk.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
-          *reinterpret_cast<u32x2*>(dst + 16 * cb) = pk;
-        }
-        if (cq == 0 && j == 0) a.lse[orow] = lse_v;
-      } else {
-        const int64_t prow = (int64_t)slot * RG + WR * hh + h;
-        _Float16* dst = a.ws_o + prow * D_C + 128 * cq + 4 * j;
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          const float4v o = O[cb][k] * inv;
-          u32x2 pk;
-          pk.x = as_u32((half2v){(_Float16)o[0], (_Float16)o[1]});
-          pk.y = as_u32((half2v){(_Float16)o[2], (_Float16)o[3]});
-          *reinterpret_cast<u32x2*>(dst + 16 * cb) = pk;
-        }
-        if (cq == 0 && j == 0) a.ws_lse[prow] = lse_v;
-      }
-    }
+    if (kh == 0 && j == 0) a.ws_lse[prow] = lse_v;
   }
   __syncthreads();  // LDS is reused by the next segment
 }
@@ -551,6 +508,8 @@ __global__ __launch_bounds__(NT, 1) void decode_wide_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  // the z tile's padding words stay zero
+  for (int i = tid; i < ST * ZW; i += NT) sm.zop[i] = 0u;
   const int nc_all = gridDim.x >> 1;
   const int c = (int)blockIdx.x % nc_all, hh = (int)blockIdx.x / nc_all;
   const int V = a.B * a.s_q;
