@@ -53,12 +53,12 @@ constexpr int ST = 32;           // tokens per step
 constexpr int NCH = 128;         // chunks of the page line (workgroups: 2 NCH)
 constexpr int NB = NG_C + NG_R;  // 18 blocks of 32 channels per token ([c | k_rope])
 constexpr int KH = 9;            // blocks per K half: content 8 kh .. 8 kh + 7 and RoPE block kh
-// Row strides in halves. Code tile: 292 dwords (36 mod 64), so 16 consecutive
-// token rows read or written 16 bytes per lane hit distinct banks. Value tile:
-// 268 dwords (12 mod 64), distinct banks for 16 consecutive rows of 16-byte
-// stores and for the 4 consecutive rows of a transposing read.
-constexpr int CT = D_ALL + 8;
-constexpr int VT = D_C + 24;
+// Row strides in halves, chosen by measuring LDS bank conflicts and the v3
+// step time over a range of paddings: code tile 312 dwords, value tile 264
+// dwords (8 mod 64: the 8 consecutive rows of 8 dwords that a transposing read
+// serves per cycle cover the 64 banks once).
+constexpr int CT = D_ALL + 48;
+constexpr int VT = D_C + 16;
 // z tile row: 8 words per block quarter q (the (z, z) words of content blocks
 // 4q .. 4q + 3, then RoPE block q for q < 2), padded to 36 words (36 mod 64:
 // 16 consecutive rows hit distinct banks); scale tile rows are ordered the
@@ -322,15 +322,19 @@ __device__ __forceinline__ void segment(WideLds& sm, const DecodeArgs& a, const 
   const int j = lane >> 4, t16 = lane & 15;
   const int hb = w & 3, kh = w >> 2;
   const int crow = 16 * (w >> 2) + t16, cq = w & 3;  // converter: token row, block quarter
-  const int* ptab = a.page_table + (int64_t)b * a.max_pages;
   auto step_p0 = [&](int st) { return PAGE * (i_begin + (st >> 1)) + ST * (st & 1); };
-  auto step_rsrc = [&](int st) {
-    const int pid = __builtin_amdgcn_readfirstlane(
-        st < n_steps ? *(const_i32*)(ptab + i_begin + (st >> 1)) : 0);
-    return page_rsrc<F>(a.pages, pid, st < n_steps);
+  // Page ids come through vector loads (in order with the code loads, so a
+  // prefetched id is waited for precisely; a scalar load would be waited for
+  // with every LDS access after it), two iterations ahead of their use.
+  const __amdgpu_buffer_rsrc_t pt_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.page_table + (int64_t)b * a.max_pages), (short)0, a.max_pages * 4, 0x00020000);
+  auto pid_load = [&](int st) {  // page id of step st (0 past the page table: range-checked offset)
+    return __builtin_amdgcn_raw_buffer_load_b32(pt_rs, 4 * (i_begin + (st >> 1)), 0, 0);
   };
-  auto load_step = [&](ConvRaw& r, int st) {
-    conv_load<F>(r, step_rsrc(st), ST * (st & 1) + crow, j, cq);
+  auto load_step = [&](ConvRaw& r, int st, uint32_t pid) {
+    const __amdgpu_buffer_rsrc_t rs =
+        page_rsrc<F>(a.pages, __builtin_amdgcn_readfirstlane(pid), st < n_steps);
+    conv_load<F>(r, rs, ST * (st & 1) + crow, j, cq);
   };
   auto convert_step = [&](const ConvRaw& r, int st) {
     const int p0 = step_p0(st);
@@ -377,10 +381,11 @@ __device__ __forceinline__ void segment(WideLds& sm, const DecodeArgs& a, const 
 
   // ---- raw codes of steps of parity 0 and 1, loaded two iterations ahead ----
   ConvRaw raw0, raw1;
-  load_step(raw0, 0);
-  load_step(raw1, 1);
+  load_step(raw0, 0, pid_load(0));
+  load_step(raw1, 1, pid_load(1));
   convert_step(raw0, 0);
-  load_step(raw0, 2);
+  load_step(raw0, 2, pid_load(2));
+  uint32_t pid1 = pid_load(3), pid0 = pid_load(4);  // next ids for raw1 / raw0
   float4v O[16];  // channel 256 kh + 16 cb + 4 j + i of head t16
 #pragma unroll
   for (int cb = 0; cb < 16; ++cb) O[cb] = (float4v){0.f, 0.f, 0.f, 0.f};
@@ -391,10 +396,11 @@ __device__ __forceinline__ void segment(WideLds& sm, const DecodeArgs& a, const 
   __syncthreads();  // step 0 converted
 
   // One iteration; rnext holds the raw codes of step it + 1 and is reloaded
-  // with step it + 3 (the loads are unconditional: past the last step the page
-  // descriptor has an empty range). Called with raw1 and raw0 in turn, so each
-  // prefetch lands in fixed registers.
-  auto iteration = [&](int it, ConvRaw& rnext) {
+  // with step it + 3, whose page id pnext was loaded two iterations ago (the
+  // loads are unconditional: past the last step the page descriptor has an
+  // empty range). Called with raw1 and raw0 in turn, so each prefetch lands in
+  // fixed registers.
+  auto iteration = [&](int it, ConvRaw& rnext, uint32_t& pnext) {
     const int buf = it & 1;
     const int p0 = step_p0(it);
     float4v S[2];
@@ -460,12 +466,13 @@ __device__ __forceinline__ void segment(WideLds& sm, const DecodeArgs& a, const 
     // this step are done) and the other value buffer (last read by the PV
     // product of step it - 1)
     if (it + 1 < n_steps) convert_step(rnext, it + 1);
-    load_step(rnext, it + 3);
+    load_step(rnext, it + 3, pnext);
+    pnext = pid_load(it + 5);
     __syncthreads();  // step it + 1 converted; every wave is done with the partials
   };
   for (int it = 0; it < n_steps; it += 2) {
-    iteration(it, raw1);
-    if (it + 1 < n_steps) iteration(it + 1, raw0);
+    iteration(it, raw1, pid1);
+    if (it + 1 < n_steps) iteration(it + 1, raw0, pid0);
   }
 
   // ---- normalize and write: out directly, or a partial for the combine ----
