@@ -13,6 +13,8 @@ CPU oracle on the same seeded inputs.
 * other sink / window sizes (none, a page-wide sink, a five-page window,
   single tokens), including a serving step that opens new pages.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -193,31 +195,39 @@ def test_decode_single_range_writes_output_directly():
     assert_decode_ok(out, lse, ref, ref_lse, label="single range")
 
 
-def test_decode_rescales_when_scores_jump():
-    """Keys of later tokens scaled up so their scores exceed the running
-    reference max by far more than the lazy-rescale threshold mid-sequence
-    (and inside one page range): the shared max moves, O and l are rescaled."""
+@pytest.mark.parametrize("H", [16, 128])
+def test_decode_rescales_when_scores_jump(H):
+    """RoPE keys of later tokens scaled up so their scores exceed the running
+    reference max by far more than the lazy-rescale threshold (2^8)
+    mid-sequence and inside one page range: the reference max moves, O and l
+    are rescaled. Token 1500 sits in the second half of a 32-token step, so at
+    H = 128 one token block of that step moves its max and the other does not.
+    Only the RoPE part is scaled: the content latent is also the value, and
+    larger values would only test the fp16 rounding of the value tile."""
     cfg = _cfg(4)
     lens = [3000, 700]
-    inp = synth.build_cache_inputs(lens, 16, seed=23, device="cpu")
-    c = inp.c_kv.float()
+    inp = synth.build_cache_inputs(lens, H, seed=23, device="cpu")
     k = inp.k_rope.float()
     # tokens 1500.. of sequence 0 and 400.. of sequence 1 (packed and window)
-    big = torch.zeros(c.shape[0], dtype=torch.bool)
+    big = torch.zeros(k.shape[0], dtype=torch.bool)
     big[1500:3000] = True
     big[3000 + 400:] = True
-    c[big] *= 12.0
     k[big] *= 12.0
-    inp.c_kv = c.to(torch.bfloat16)
     inp.k_rope = k.to(torch.bfloat16)
-    print("[case] decode score jumps", flush=True)
+    # the jump, in log2 units, of every head of sequence 0 (from the unquantized
+    # inputs) is well past the threshold
+    S = (inp.q_lat[0].float() @ inp.c_kv[:3000].float().T
+         + inp.q_rope[0].float() @ k[:3000].T) * (synth.SOFTMAX_SCALE / math.log(2.0))
+    jump = S[:, 1500:].max(1).values - S[:, :1500].max(1).values
+    assert jump.min().item() > 10.0, jump.min().item()
+    print(f"[case] decode score jumps H={H}", flush=True)
     pages, sink, local = gpu_cache(cfg, inp, len(lens))
     out, lse = gpu_decode(cfg, inp, pages, sink, local)
     torch.cuda.synchronize()
     oc = ocfg_of(cfg)
     op, osink, olocal = oracle_cache(oc, inp, len(lens))
     ref, ref_lse = oracle_decode(oc, inp, op, osink, olocal, synth.SOFTMAX_SCALE)
-    assert_decode_ok(out, lse, ref, ref_lse, label="score jumps")
+    assert_decode_ok(out, lse, ref, ref_lse, label=f"score jumps H{H}")
 
 
 def test_decode_tiny_workload():
