@@ -740,9 +740,10 @@ size_t decode_workspace_bytes(int B, int H, int max_pages) {
 
 hipError_t launch_decode(DecodeArgs a, int fmt, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
-  // 128 heads per query token over a packed cache: one dequantization per
-  // page and 64 heads, work split by page weight (decode_wide.hip)
-  if (fmt != 16 && a.h_per_q == 128) return launch_decode_wide(a, a.ws_lse, fmt, stream);
+  // 128 heads per query token: one dequantization (or, for BF16 pages, one
+  // conversion to fp16) per page and 64 heads, work split by page weight
+  // (decode_wide.hip)
+  if (a.h_per_q == 128) return launch_decode_wide(a, a.ws_lse, fmt, stream);
   const int n_u = a.B * a.n_split;
   const dim3 grid((n_u + 7) / 8 * 8 * (a.H / 16));
   if (fmt == 16) {

@@ -39,6 +39,12 @@
 //            256 kh .. 256 kh + 255 (64 accumulators per lane), V^T read
 //            transposed (ds_read_b64_tr_b16), P the B operand.
 // Two barriers per step (partial scores ready; next step converted).
+//
+// The same kernel decodes the paired BF16 cache the pages normalize their
+// latency to (Figure 5(b), Table 9) at 128 heads: its pages' rows enter the
+// value buffer as fp16 (exact), and the scores are one plain MFMA chain over
+// the values, with no scales, zero points or code tile; chunking, softmax, PV
+// and combine are the packed cache's.
 #include "mla_common.h"
 #include "mla_kernels.h"
 #include "decode_ops.h"
@@ -153,17 +159,35 @@ __device__ __forceinline__ int owner(int64_t u, int64_t W, int nc) {
 // for its channel quarter cq: the content codes of groups 4 cq .. 4 cq + 3
 // (C4: one 16-byte chunk; C2: two words), their (scale, zero) words, and for
 // cq < 2 the code word and (scale, zero) word of RoPE group cq.
+template <int F>
 struct ConvRaw {
   u32x4 c, s;
   uint32_t r, rs;
+};
+// BF16 pages (the paired baseline): the lane's 8 channels of content blocks
+// 4 cq .. 4 cq + 3 and of RoPE block cq & 1, as stored
+template <>
+struct ConvRaw<16> {
+  u32x4 c[4];
+  u32x4 r;
 };
 
 // (A group of 2 or 4 blocks has one (scale, zero) word: it is repeated for
 // each of its blocks, so the tiles always hold one word per block.)
 template <int F>
-__device__ __forceinline__ void conv_load(ConvRaw& t, __amdgpu_buffer_rsrc_t rs, int slot, int j,
+__device__ __forceinline__ void conv_load(ConvRaw<F>& t, __amdgpu_buffer_rsrc_t rs, int slot, int j,
                                           int cq) {
   using G = PageGeom<F>;
+  if constexpr (F == 16) {
+    // token rows of 576 bf16: block g, sub-block j at bytes 64 g + 16 j
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      t.c[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rs, slot * G::ROW + 64 * (4 * cq + e) + 16 * j, 0, 0));
+    t.r = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        rs, slot * G::ROW + 2 * D_C + 64 * (cq & 1) + 16 * j, 0, 0));
+    return;
+  } else {
   if constexpr (G::CB == 4) {
     t.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                         rs, slot * G::CC + 16 * j + 64 * cq, G::OFF_CC, 0));
@@ -191,6 +215,7 @@ __device__ __forceinline__ void conv_load(ConvRaw& t, __amdgpu_buffer_rsrc_t rs,
                    : __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::RC + 4 * j, G::OFF_RC, 0);
   t.rs = __builtin_amdgcn_raw_buffer_load_b32(rs, slot * G::RS + (G::GMR == 1 ? 4 * rq : 0),
                                               G::OFF_RS, 0);
+  }
 }
 
 // One converter lane's share of a step (token row `row` of the step, sub-block
@@ -201,14 +226,27 @@ __device__ __forceinline__ void conv_load(ConvRaw& t, __amdgpu_buffer_rsrc_t rs,
 // BF16 row (brow) takes its values with (scale, zero) = (1, 0); an invalid
 // token zeros.
 template <int F>
-__device__ __forceinline__ void convert_tok(const ConvRaw& t, WideLds& sm, int buf, int row, int j,
+__device__ __forceinline__ void convert_tok(const ConvRaw<F>& t, WideLds& sm, int buf, int row, int j,
                                             int cq, bool mixed, bool valid, const uint16_t* brow) {
-  u32x4 sw = t.s;
-  uint32_t rsw = t.rs;
+  u32x4 sw;
+  uint32_t rsw;
   half8 c[4], r;
+  if constexpr (F == 16) {
+    // BF16 rows enter as fp16 values (exact) with (scale, zero) = (1, 0)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) c[e] = fmt_cb(F) == 4 ? codes4(t.c[e]) : codes2(t.c[e >> 1], e & 1);
-  r = fmt_rb(F) == 4 ? codes4(t.r) : codes2(t.r, cq & 1);
+    for (int e = 0; e < 4; ++e) {
+      c[e] = bf16x8_to_f16x8(t.c[e]);
+      sw[e] = 0x00003C00u;
+    }
+    r = bf16x8_to_f16x8(t.r);
+    rsw = 0x00003C00u;
+  } else {
+    sw = t.s;
+    rsw = t.rs;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[e] = fmt_cb(F) == 4 ? codes4(t.c[e]) : codes2(t.c[e >> 1], e & 1);
+    r = fmt_rb(F) == 4 ? codes4(t.r) : codes2(t.r, cq & 1);
+  }
   if (mixed) {
     if (brow != nullptr) {
 #pragma unroll
@@ -232,6 +270,14 @@ __device__ __forceinline__ void convert_tok(const ConvRaw& t, WideLds& sm, int b
   }
   _Float16* crow = sm.code + row * CT;
   _Float16* vrow = sm.val[buf] + row * VT;
+  if constexpr (F == 16) {
+    // the values are what both products read: content into the value buffer
+    // only, RoPE into the code tile; no scales or zero points
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<half8*>(vrow + GROUP * (4 * cq + e) + 8 * j) = c[e];
+    if (cq < NG_R) *reinterpret_cast<half8*>(crow + D_C + GROUP * cq + 8 * j) = r;
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     *reinterpret_cast<half8*>(crow + GROUP * (4 * cq + e) + 8 * j) = c[e];
@@ -306,6 +352,26 @@ __device__ __forceinline__ void step_scores(const WideLds& sm, int kh,
   }
 }
 
+// Partial scores of the BF16 baseline, in the same lane layout: the values
+// (content from value buffer vt, RoPE from the code tile) are the A operand of
+// one MFMA chain over the wave's 9 blocks; there is no scale or zero point.
+__device__ __forceinline__ void step_scores_bf16(const WideLds& sm, const _Float16* vt, int kh,
+                                                 const half8 (&qA)[KH], int j, int t16,
+                                                 float4v (&S)[2]) {
+  S[0] = S[1] = (float4v){0.f, 0.f, 0.f, 0.f};
+  const _Float16* v0 = vt + t16 * VT + 8 * j;
+  const _Float16* r0 = sm.code + t16 * CT + D_C + GROUP * kh + 8 * j;
+#pragma unroll
+  for (int k = 0; k < KH; ++k) {
+    const _Float16* p = k < 8 ? v0 + GROUP * (8 * kh + k) : r0;
+    const int stride = k < 8 ? 16 * VT : 16 * CT;
+    const half8 A0 = *reinterpret_cast<const half8*>(p);
+    const half8 A1 = *reinterpret_cast<const half8*>(p + stride);
+    S[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qA[k], S[0], 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qA[k], S[1], 0, 0, 0);
+  }
+}
+
 // One segment: pages [i_begin, i_begin + n_steps / 2) of (sequence, query
 // token) v, heads 64 hh .. 64 hh + 63. Wave w scores head block hb = w & 3
 // over K half kh = w >> 2 and accumulates O^T of those 16 heads for content
@@ -331,20 +397,22 @@ __device__ __forceinline__ void segment(WideLds& sm, const DecodeArgs& a, const 
   auto pid_load = [&](int st) {  // page id of step st (0 past the page table: range-checked offset)
     return __builtin_amdgcn_raw_buffer_load_b32(pt_rs, 4 * (i_begin + (st >> 1)), 0, 0);
   };
-  auto load_step = [&](ConvRaw& r, int st, uint32_t pid) {
+  auto load_step = [&](ConvRaw<F>& r, int st, uint32_t pid) {
     const __amdgpu_buffer_rsrc_t rs =
         page_rsrc<F>(a.pages, __builtin_amdgcn_readfirstlane(pid), st < n_steps);
     conv_load<F>(r, rs, ST * (st & 1) + crow, j, cq);
   };
-  auto convert_step = [&](const ConvRaw& r, int st) {
+  auto convert_step = [&](const ConvRaw<F>& r, int st) {
     const int p0 = step_p0(st);
     const bool mixed = p0 < s.n_s || p0 + ST > min(s.lo_start, s.Lq);
     const int p = p0 + crow;
     const bool valid = p < s.Lq;
     const uint16_t* brow = nullptr;
-    if (mixed && valid && (p < s.n_s || p >= s.lo_start))
-      brow = p < s.n_s ? a.sink + ((int64_t)b * a.n_sink + p) * D_ALL
-                       : a.local + ((int64_t)b * a.n_local + p % a.n_local) * D_ALL;
+    if constexpr (F != 16) {  // the BF16 baseline has no protected buffers
+      if (mixed && valid && (p < s.n_s || p >= s.lo_start))
+        brow = p < s.n_s ? a.sink + ((int64_t)b * a.n_sink + p) * D_ALL
+                         : a.local + ((int64_t)b * a.n_local + p % a.n_local) * D_ALL;
+    }
     convert_tok<F>(r, sm, st & 1, crow, j, cq, mixed, valid, brow);
   };
 
@@ -379,8 +447,8 @@ __device__ __forceinline__ void segment(WideLds& sm, const DecodeArgs& a, const 
     }
   }
 
-  // ---- raw codes of steps of parity 0 and 1, loaded two iterations ahead ----
-  ConvRaw raw0, raw1;
+  // ---- raw data of steps of parity 0 and 1, loaded two iterations ahead ----
+  ConvRaw<F> raw0, raw1;
   load_step(raw0, 0, pid_load(0));
   load_step(raw1, 1, pid_load(1));
   convert_step(raw0, 0);
@@ -395,16 +463,17 @@ __device__ __forceinline__ void segment(WideLds& sm, const DecodeArgs& a, const 
   const int tr_hi = tr_lo + 16 * VT;
   __syncthreads();  // step 0 converted
 
-  // One iteration; rnext holds the raw codes of step it + 1 and is reloaded
+  // One iteration; rnext holds the raw data of step it + 1 and is reloaded
   // with step it + 3, whose page id pnext was loaded two iterations ago (the
   // loads are unconditional: past the last step the page descriptor has an
   // empty range). Called with raw1 and raw0 in turn, so each prefetch lands in
   // fixed registers.
-  auto iteration = [&](int it, ConvRaw& rnext, uint32_t& pnext) {
+  auto iteration = [&](int it, ConvRaw<F>& rnext, uint32_t& pnext) {
     const int buf = it & 1;
     const int p0 = step_p0(it);
     float4v S[2];
-    step_scores(sm, kh, qA, qz, j, t16, S);
+    if constexpr (F == 16) step_scores_bf16(sm, sm.val[buf], kh, qA, j, t16, S);
+    else step_scores(sm, kh, qA, qz, j, t16, S);
     sm.xs[w][0][lane] = S[0];
     sm.xs[w][1][lane] = S[1];
     __syncthreads();  // partial scores of both K halves
@@ -654,9 +723,13 @@ hipError_t launch_decode_wide(DecodeArgs a, void* workspace, int fmt, hipStream_
   a.ws_lse = reinterpret_cast<float*>(base + meta);
   a.ws_o = reinterpret_cast<_Float16*>(base + meta + slots * RG * sizeof(float));
   const dim3 grid(2 * NCH);
+  if (fmt == 16) {
+    decode_wide_kernel<16><<<grid, dim3(NT), 0, stream>>>(a);
+  } else {
 #define MLA_LAUNCH_WIDE(F) decode_wide_kernel<F><<<grid, dim3(NT), 0, stream>>>(a)
-  MLA_FOR_PACKED_FMT(fmt, MLA_LAUNCH_WIDE)
+    MLA_FOR_PACKED_FMT(fmt, MLA_LAUNCH_WIDE)
 #undef MLA_LAUNCH_WIDE
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)V * RG;

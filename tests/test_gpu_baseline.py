@@ -69,25 +69,27 @@ def test_bf16_decode_edge_lengths(H):
     assert not out[b0].float().abs().sum().item()
 
 
-def test_bf16_decode_full_v2lite_sampled():
-    """The V2-Lite-shaped batch (B8 H16 L32768) as a BF16 cache, in the bench's
-    launch configuration; sampled sequences and heads against the oracle."""
-    wl = synth.WORKLOADS["v2lite"]
-    print("[case] bf16 full v2lite: generating on the GPU", flush=True)
+@pytest.mark.parametrize("name", ["v2lite", "v3"])
+def test_bf16_decode_full_sampled(name):
+    """The V2-Lite-shaped (B8 H16 L32768) and V3-shaped (B32 H128 L8192, the
+    64-head kernel) batches as a BF16 cache, in the bench's launch
+    configuration; sampled sequences and heads against the oracle."""
+    wl = synth.WORKLOADS[name]
+    print(f"[case] bf16 full {name}: generating on the GPU", flush=True)
     inp, _ = synth.workload_inputs(wl, device=DEV)
     pages = mla.allocate_bf16_cache(inp.num_pages, DEV)
     mla.bf16_write(inp.c_kv, inp.k_rope, inp.seq_idx, inp.pos, inp.page_table, pages)
     out, lse = mla.bf16_decode(inp.q_lat, inp.q_rope, pages, inp.page_table, inp.seq_lens,
                                synth.SOFTMAX_SCALE)
     torch.cuda.synchronize()
-    print("[case] bf16 full v2lite: GPU done, oracle on sampled rows", flush=True)
+    print(f"[case] bf16 full {name}: GPU done, oracle on sampled rows", flush=True)
     rng = np.random.default_rng(3)
     seqs = [0, 5]
     rows = [(b, int(h)) for b in seqs for h in sorted(rng.choice(wl.H, 6, replace=False))]
     ref, ref_lse = oracle.bf16_decode(oracle.Cfg(), synth.SOFTMAX_SCALE, u16(inp.q_lat),
                                       u16(inp.q_rope), u16(pages), inp.page_table.cpu().numpy(),
                                       inp.seq_lens.cpu().numpy(), sel=rows)
-    assert_decode_ok(out, lse, ref, ref_lse, rows=rows, label="bf16 v2lite")
+    assert_decode_ok(out, lse, ref, ref_lse, rows=rows, label=f"bf16 {name}")
     # the sampled sequences' pages hold exactly their token rows
     op = np.zeros((inp.num_pages, 64, 576), np.uint16)
     mask = torch.zeros(inp.seq_idx.numel(), dtype=torch.bool, device=DEV)
