@@ -548,10 +548,10 @@ def paired_bf16(args, wl, inp, t_lowbit_us, lowbit_cache_bytes, step=None):
     print(f"[bench] paired BF16 cache: {t_bf16:.1f} us/step events "
           f"({bw:.0f} GB/s algorithmic)", file=sys.stderr, flush=True)
     tr = measured_traffic(wl.name, "bf16_decode") if step is None else None
-    return {"kernel": ("mla_bf16_decode: decode_kernel<BF16 pages> + combine_kernel"
-                       if step is None else
-                       "mla_bf16_write + mla_bf16_decode: write_bf16_kernel + decode_kernel<BF16 "
-                       "pages> + combine_kernel"),
+    dec = ("decode_wide_kernel<BF16 pages> + combine_wide_kernel" if wl.H == 128
+           else "decode_kernel<BF16 pages> + combine_kernel")
+    return {"kernel": (f"mla_bf16_decode: {dec}" if step is None else
+                       f"mla_bf16_write + mla_bf16_decode: write_bf16_kernel + {dec}"),
             "event_us_mean": round(t_bf16, 2), "hbm_frac": round(bw / PEAK_HBM_GBS, 4),
             "traffic": tr["bytes_per_call"] if tr else None,
             "delta_pct": round((t_lowbit_us / t_bf16 - 1.0) * 100.0, 2),
