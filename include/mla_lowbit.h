@@ -268,10 +268,11 @@ int mla_lowbit_qdq(const mla_lowbit_config* cfg, int n_tokens, const void* c_kv,
  * 64 rows of [c_kv (512) | k_rope (64)] bf16 (73728 bytes); no sink or local
  * buffers. The decode runs the same kernel skeleton as mla_lowbit_decode
  * (page ranges, or at 128 heads the length-aware chunks; one softmax,
- * log-sum-exp merge) without the unpacking: at 16 heads per query token the
- * scores are bf16 MFMA on the rows as stored, at 128 heads one fp16 MFMA
- * chain over the rows converted to fp16. The product with P is in fp16 in
- * both, so the same fp16-range precondition as for the packed cache applies:
+ * log-sum-exp merge) without the unpacking: with 128 heads per query token
+ * the scores are one fp16 MFMA chain over the rows converted to fp16, with
+ * any other head count bf16 MFMA on the rows as stored. The product with P
+ * is in fp16 in both, so the fp16-range precondition of the packed cache
+ * applies:
  * |x| <= 65504 for every cached value, and values below 2^-14 keep only the
  * bits an fp16 subnormal holds.
  */
