@@ -64,6 +64,50 @@ __device__ __forceinline__ void group_extremes(float& lo, float& hi, int j) {
   if constexpr (GM >= 4) mirror_merge<0x140, 8>(lo, hi, j);
 }
 
+// The same extremes without the order of equal values (min / max over the
+// group's 4 GM lanes, partners by DPP as in group_extremes). The hardware
+// min / max are written out: the library forms would first quiet signaling
+// NaNs, which the inputs (finite by the writer's contract) never hold.
+__device__ __forceinline__ float vmin3(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmin2(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int GM>
+__device__ __forceinline__ void group_minmax(float& lo, float& hi) {
+  lo = vmin2(lo, dpp_f<0xB1>(lo));
+  hi = vmax2(hi, dpp_f<0xB1>(hi));
+  lo = vmin2(lo, dpp_f<0x4E>(lo));
+  hi = vmax2(hi, dpp_f<0x4E>(hi));
+  if constexpr (GM >= 2) {
+    lo = vmin2(lo, dpp_f<0x141>(lo));
+    hi = vmax2(hi, dpp_f<0x141>(hi));
+  }
+  if constexpr (GM >= 4) {
+    lo = vmin2(lo, dpp_f<0x140>(lo));
+    hi = vmax2(hi, dpp_f<0x140>(hi));
+  }
+}
+
 // Asymmetric min-max quantization of one group of 32 GM channels held by
 // 4 GM lanes (lane j of the group: channels 8j .. 8j + 7 in raw, bf16): fp16
 // scale s = (hi - lo) / (2^bits - 1) and zero z = lo (both rounded to nearest
@@ -79,13 +123,24 @@ __device__ __forceinline__ void quantize8(const u32x4& raw, int bits, int j, _Fl
     x[2 * e] = bf16_to_f32(raw[e] & 0xffffu);
     x[2 * e + 1] = bf16_to_f32(raw[e] >> 16);
   }
-  float lo = x[0], hi = x[0];
+  // The group's extremes: min / max over the lanes' values (v_min3 / v_max3,
+  // then min / max with the DPP partners). Equal values only differ in bits
+  // when they are zeros of opposite sign, so where an extreme is a zero the
+  // wavefront takes the ordered scan instead, in which the first of equal
+  // values wins.
+  float lo = vmin2(vmin3(vmin3(x[0], x[1], x[2]), x[3], x[4]), vmin3(x[5], x[6], x[7]));
+  float hi = vmax2(vmax3(vmax3(x[0], x[1], x[2]), x[3], x[4]), vmax3(x[5], x[6], x[7]));
+  group_minmax<GM>(lo, hi);
+  if (__builtin_amdgcn_ballot_w64(lo == 0.0f || hi == 0.0f) != 0) {
+    lo = x[0];
+    hi = x[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) {  // strict compares: the first of equal values wins
-    lo = x[i] < lo ? x[i] : lo;
-    hi = x[i] > hi ? x[i] : hi;
+    for (int i = 1; i < 8; ++i) {  // strict compares: the first of equal values wins
+      lo = x[i] < lo ? x[i] : lo;
+      hi = x[i] > hi ? x[i] : hi;
+    }
+    group_extremes<GM>(lo, hi, j);
   }
-  group_extremes<GM>(lo, hi, j);
   const float qmax = (float)((1 << bits) - 1);
   s16 = (_Float16)__fdiv_rn(__fsub_rn(hi, lo), qmax);  // nearest even
   z16 = (_Float16)lo;
@@ -99,7 +154,8 @@ __device__ __forceinline__ void quantize8(const u32x4& raw, int bits, int j, _Fl
   // as a per-lane select they would all be executed).
   // (t is within 1e-5 of a half-integer exactly when |t - rint(t)| > 0.5 - 1e-5;
   // the subtraction is exact for |t| <= 17.)
-  const float rs = __builtin_amdgcn_rcpf(s);
+  // (s = 0: rs = 0 makes every quotient 0, hence every code 0)
+  const float rs = s != 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
   float d[8], r[8];
   bool near = false;
 #pragma unroll
@@ -109,7 +165,6 @@ __device__ __forceinline__ void quantize8(const u32x4& raw, int bits, int j, _Fl
     r[i] = rintf(t);
     near |= __builtin_fabsf(t - r[i]) > 0.5f - 1e-5f;
   }
-  near = near && s != 0.0f;
   if (__builtin_amdgcn_ballot_w64(near) != 0) {
     if (near) {
 #pragma unroll
@@ -120,8 +175,7 @@ __device__ __forceinline__ void quantize8(const u32x4& raw, int bits, int j, _Fl
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    q[i] = s != 0.0f ? (uint32_t)__builtin_amdgcn_fmed3f(r[i], 0.0f, qmax) : 0u;
+  for (int i = 0; i < 8; ++i) q[i] = (uint32_t)__builtin_amdgcn_fmed3f(r[i], 0.0f, qmax);
 }
 
 // Quantize and store the 8 channels (sub-block j of 32-channel block gi) one
